@@ -1,0 +1,226 @@
+"""Plain, slow, obviously correct CPU oracle of the W4A16 group-quantized GEMM.
+
+Test infrastructure only: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` use it.  It shares no code with the HIP
+library and imports nothing from it.
+
+What is computed, and where the pages state it
+----------------------------------------------
+Pages are cited by title and section:
+
+* "The Silence of Success: A Single Line That Speaks Volumes", section "What
+  the Edit Actually Built": fp32 activations times int4 weights held two
+  4-bit values per byte, one scale per group of 32 input columns; the golden
+  result is numpy's dequantize-then-multiply.
+* "The Quiet Commit: How a Single Documentation Edit Marks the Completion of
+  a Major Engineering Milestone", section "The INT4 Milestone": symmetric
+  quantization, 8 nibbles per int32 along the input dimension, value =
+  nibble - 8, fp32 per-group scales; golden outputs computed from the
+  dequantized weights.  Section "Input Knowledge Required" repeats group 32,
+  8 nibbles per int32 and value = nibble - 8.
+* "The Quiet Commit: How a Single Plan Update Closed Phase 3 of a Native DDTree
+  Inference Engine", section "The Context: Phase 3 of a Custom Inference
+  Stack": symmetric per-group quantization, group 32, 8 nibbles per int32
+  along the input dimension.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* Layout: W is [N][K] (N outputs, K inputs), Y = X . dequant(W)^T.
+  ``qweight[n][j]`` holds k = 8j + i in bits 4i..4i+3, i = 0..7, low nibble
+  first; on a little-endian machine byte b of the word then holds k = 8j+2b
+  (low half) and 8j+2b+1 (high half), which is the "two 4-bit values per
+  byte" the first page describes.  Unpacking uses logical shifts on the
+  unsigned word (a word whose nibble 7 is >= 8 is negative as int32).
+* Scale: scale = max|w| / 7 over the group, one fp32 true division rounded
+  to nearest even.
+* Code: q = clamp(rint(w / scale), -8, 7) with an fp32 true division and
+  round-half-to-even; nibble = q + 8.  A group whose scale is 0 (all zero,
+  or so tiny that max|w|/7 underflows) gets q = 0 everywhere.
+* Non-finite weights are rejected; K % 32 != 0 is rejected (no padding).
+* Dequantized weight = fl32((nibble - 8) * scale), one rounded fp32 multiply.
+* Product: accumulated in fp64 (every fp32 x fp32 product is exact in fp64).
+  An fp32 result is accepted iff |Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6
+  elementwise, with w the dequantized fp32 weight and the sum in fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+REL_TOL = 1e-5
+ABS_TOL = 1e-6
+
+_F32 = np.float32
+
+
+def check_k(K: int) -> None:
+    """K must be a positive multiple of the group width (no padding path)."""
+    if K <= 0 or K % GROUP != 0:
+        raise ValueError(f"K={K} is not a positive multiple of {GROUP}")
+
+
+# --------------------------------------------------------------------------
+# quantize: "symmetric per-group quantization, group size 32"
+# --------------------------------------------------------------------------
+
+def quantize(W: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """W fp32 [N][K] -> (qweight int32 [N][K/8], scales fp32 [N][K/32]).
+
+    Steps, in order: group the K axis in runs of 32; scale = max|w| / 7 (fp32);
+    q = rint(w / scale) (fp32 division, ties to even), clamped to [-8, 7];
+    nibble = q + 8; pack 8 nibbles per word, low nibble first.
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float32 or W.ndim != 2:
+        raise TypeError("W must be a 2-D float32 array")
+    N, K = W.shape
+    check_k(K)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
+    G = K // GROUP
+    Wg = W.reshape(N, G, GROUP)
+    amax = np.max(np.abs(Wg), axis=2)                 # exact
+    scale = (amax / _F32(7.0)).astype(np.float32)     # fp32 true division
+    zero = scale == 0
+    safe = np.where(zero, _F32(1.0), scale).astype(np.float32)
+    ratio = (Wg / safe[:, :, None]).astype(np.float32)  # fp32 true division
+    q = np.rint(ratio)                                 # round half to even
+    q = np.where(zero[:, :, None], _F32(0.0), q)
+    q = np.clip(q, -8, 7)
+    nib = (q.astype(np.int64) + 8).astype(np.uint8).reshape(N, K)
+    return pack(nib), scale
+
+
+# --------------------------------------------------------------------------
+# pack / unpack: "8 nibbles per int32 along the input dimension"
+# --------------------------------------------------------------------------
+
+def pack(nib: np.ndarray) -> np.ndarray:
+    """nibbles [N][K] (values 0..15) -> int32 [N][K/8], nibble i of word j = k 8j+i."""
+    nib = np.asarray(nib)
+    N, K = nib.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8 to pack")
+    if np.any((nib.astype(np.int64) < 0) | (nib.astype(np.int64) > 15)):
+        raise ValueError("nibble out of range")
+    words = np.zeros((N, K // 8), dtype=np.uint64)
+    for i in range(8):
+        words |= nib[:, i::8].astype(np.uint64) << np.uint64(4 * i)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def unpack(qweight: np.ndarray) -> np.ndarray:
+    """int32 [N][K/8] -> nibbles uint8 [N][K] (logical shifts on the unsigned word)."""
+    u = np.asarray(qweight, dtype=np.int32).view(np.uint32)
+    N, J = u.shape
+    nib = np.empty((N, 8 * J), dtype=np.uint8)
+    for i in range(8):
+        nib[:, i::8] = ((u >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.uint8)
+    return nib
+
+
+# --------------------------------------------------------------------------
+# dequantize: "value = nibble - 8", times the group's fp32 scale
+# --------------------------------------------------------------------------
+
+def dequantize(qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp32 [N][K] with w = fl32((nibble - 8) * scale[n][k // 32])."""
+    nib = unpack(qweight)
+    N, K = nib.shape
+    scales = np.asarray(scales, dtype=np.float32)
+    if scales.shape != (N, K // GROUP):
+        raise ValueError(f"scales shape {scales.shape} != {(N, K // GROUP)}")
+    centred = nib.astype(np.float32) - _F32(8.0)             # exact small integers
+    s = np.repeat(scales, GROUP, axis=1)                       # scale of k's group
+    return (centred * s).astype(np.float32)                    # one fp32 multiply
+
+
+# --------------------------------------------------------------------------
+# the product, accumulated in fp64 ("dequantize-then-multiply")
+# --------------------------------------------------------------------------
+
+def _operands(X, qweight, scales):
+    X = np.asarray(X)
+    if X.dtype != np.float32 or X.ndim != 2:
+        raise TypeError("X must be a 2-D float32 array")
+    check_k(X.shape[1])
+    Wd = dequantize(qweight, scales)
+    if Wd.shape[1] != X.shape[1]:
+        raise ValueError("K of X and of the weights differ")
+    return X, Wd
+
+
+def gemm(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Y_ref[M][N] = X . dequant(W)^T, every product and sum in fp64."""
+    X, Wd = _operands(X, qweight, scales)
+    return X.astype(np.float64) @ Wd.astype(np.float64).T
+
+
+def abs_gemm(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """T[M][N] = sum_k |x_k| |w_k| in fp64 (the scale of the tolerance)."""
+    X, Wd = _operands(X, qweight, scales)
+    return np.abs(X).astype(np.float64) @ np.abs(Wd).astype(np.float64).T
+
+
+def gemm_entries(X, qweight, scales, rows, cols):
+    """(Y_ref, T) at the listed (row, col) pairs only, one dot product each.
+
+    For full-size problems where the whole fp64 product would be slow: each
+    entry dequantizes one weight row and takes one fp64 dot product.
+    """
+    X = np.asarray(X)
+    check_k(X.shape[1])
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    y = np.empty(rows.shape, dtype=np.float64)
+    t = np.empty(rows.shape, dtype=np.float64)
+    cache = {}
+    for idx, (m, n) in enumerate(zip(rows.tolist(), cols.tolist())):
+        if n not in cache:
+            cache[n] = dequantize(qweight[n:n + 1], scales[n:n + 1])[0].astype(np.float64)
+        w = cache[n]
+        x = X[m].astype(np.float64)
+        y[idx] = float(np.dot(x, w))
+        t[idx] = float(np.dot(np.abs(x), np.abs(w)))
+    return y, t
+
+
+# --------------------------------------------------------------------------
+# acceptance
+# --------------------------------------------------------------------------
+
+def bound(T: np.ndarray) -> np.ndarray:
+    """Allowed |Y - Y_ref|: 1e-5 * sum_k |x_k w_k| + 1e-6."""
+    return REL_TOL * np.asarray(T, dtype=np.float64) + ABS_TOL
+
+
+def _verdict(Y, Yref, T) -> dict:
+    Y = np.asarray(Y, dtype=np.float64)
+    err = np.abs(Y - Yref)
+    ratio = err / bound(T)
+    finite = bool(np.all(np.isfinite(Y)))
+    worst = float(np.max(ratio)) if ratio.size else 0.0
+    return {
+        "ok": finite and worst <= 1.0,
+        "max_ratio": worst,
+        "max_abs_err": float(np.max(err)) if err.size else 0.0,
+        "finite": finite,
+        "n": int(ratio.size),
+    }
+
+
+def compare(Y: np.ndarray, X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> dict:
+    """Check every element of an fp32 result against the fp64 oracle."""
+    Yref = gemm(X, qweight, scales)
+    T = abs_gemm(X, qweight, scales)
+    if np.shape(Y) != Yref.shape:
+        raise ValueError(f"Y shape {np.shape(Y)} != {Yref.shape}")
+    return _verdict(Y, Yref, T)
+
+
+def compare_entries(Y: np.ndarray, X, qweight, scales, rows, cols) -> dict:
+    """Check sampled entries Y[rows[i], cols[i]] against the oracle."""
+    Yref, T = gemm_entries(X, qweight, scales, rows, cols)
+    got = np.asarray(Y)[np.asarray(rows), np.asarray(cols)]
+    return _verdict(got, Yref, T)

@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the W4A16 group-quantized GEMM.
+
+This module only draws random numbers.  It holds none of the method's
+arithmetic (no quantization, packing, dequantization or matrix product), so
+both the CPU oracle and the HIP path may take their inputs from it without
+sharing any code of the method.
+
+Every array is drawn with ``numpy.random.default_rng(seed)`` in float64 and
+cast to float32 last.  Draw order is fixed: X first, then W, then any mask.
+
+The workload shapes stand in for the layers the pages run through the INT4
+path (MoE experts, shared expert and dense MLP of a DeepSeek-V3/Kimi-style
+model: "The Quiet Commit ... Documentation Edit", section "The INT4
+Milestone").  The pages measure no public benchmark or dataset; these
+synthetic draws replace the tiny model bundles and real weights they used.
+"""
+
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass
+
+import numpy as np
+
+GROUP = 32  # group width along K (format constant of the weights)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    K: int
+    N: int
+    seed: int
+    x_kind: str  # "gauss", "half_gauss" or "correlated"
+    w_kind: str  # "gauss" or "outlier"
+    note: str
+
+    @property
+    def groups(self) -> int:
+        return self.K // GROUP
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the GEMM must move once: packed weights, scales, X and Y."""
+        M, N, K = self.M, self.N, self.K
+        return N * K // 2 + 4 * N * (K // GROUP) + 4 * M * K + 4 * M * N
+
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 256, 512, 0, "gauss", "gauss",
+                     "tiny check, fits in cache"),
+    "decode_gate_up": Workload("decode_gate_up", 1, 7168, 4096, 1, "gauss", "gauss",
+                               "decode GEMV, MoE gate+up projection (2x2048)"),
+    "decode_down": Workload("decode_down", 1, 2048, 7168, 2, "half_gauss", "outlier",
+                            "decode GEMV, MoE down projection, 1% x10 weight outliers"),
+    "verify_tree": Workload("verify_tree", 64, 7168, 4096, 3, "correlated", "gauss",
+                            "draft-tree verify batch of 64 correlated tokens"),
+    "prefill": Workload("prefill", 4096, 7168, 4096, 4, "gauss", "gauss",
+                        "prefill-shaped GEMM"),
+}
+
+ORDER = ["tiny", "decode_gate_up", "decode_down", "verify_tree", "prefill"]
+
+
+def _draw_x(rng: np.random.Generator, kind: str, M: int, K: int) -> np.ndarray:
+    if kind == "gauss":
+        x = rng.standard_normal((M, K))
+    elif kind == "half_gauss":
+        x = 0.5 * rng.standard_normal((M, K))
+    elif kind == "correlated":
+        base = rng.standard_normal(K)
+        noise = rng.standard_normal((M, K))
+        x = base[None, :] + 0.1 * noise
+    else:
+        raise ValueError(f"unknown activation kind {kind!r}")
+    return x.astype(np.float32)
+
+
+def _draw_w(rng: np.random.Generator, kind: str, N: int, K: int) -> np.ndarray:
+    w = 0.02 * rng.standard_normal((N, K))
+    if kind == "outlier":
+        mask = rng.random((N, K)) < 0.01
+        w[mask] *= 10.0
+    elif kind != "gauss":
+        raise ValueError(f"unknown weight kind {kind!r}")
+    return w.astype(np.float32)
+
+
+def make(name: str) -> tuple[np.ndarray, np.ndarray]:
+    """Return (X[M][K], W[N][K]) float32 for a named workload."""
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(wl.seed)
+    x = _draw_x(rng, wl.x_kind, wl.M, wl.K)
+    w = _draw_w(rng, wl.w_kind, wl.N, wl.K)
+    return x, w
+
+
+def make_w(name: str) -> np.ndarray:
+    """W only, drawn after X exactly as make() draws it."""
+    return make(name)[1]
+
+
+def random_case(M: int, N: int, K: int, seed: int, x_kind: str = "gauss",
+                w_kind: str = "gauss") -> tuple[np.ndarray, np.ndarray]:
+    """(X, W) of an arbitrary shape, same recipe as the named workloads."""
+    rng = np.random.default_rng(seed)
+    return _draw_x(rng, x_kind, M, K), _draw_w(rng, w_kind, N, K)
+
+
+def integer_case(M: int, N: int, K: int, seed: int, lo: int = -8, hi: int = 8):
+    """Integer-valued X in [lo, hi] and raw nibbles in [0, 15], as float32 / uint8.
+
+    Used for the exact special case: with one power-of-two scale for every
+    group, every partial sum of the product is an integer multiple of that
+    scale far below 2**24, so any summation order is exact in fp32.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
+    nib = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    return x, nib
+
+
+def random_words(shape, seed: int) -> np.ndarray:
+    """Uniform random int32 words (all bit patterns, negatives included)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(-(2 ** 31), 2 ** 31, size=shape, dtype=np.int64).astype(np.int32)
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
