@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 group-quantized GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu]
+
+A step is one call of w4a16_gemm (the whole hot path: validate, launch,
+unpack + dequant + fp32 contraction + reduction + store) on one batch of
+synthetic input.  Inputs are resident in HBM before the timed region starts.
+Copies of {X, qweight, scales, Y} rotate so that every step reads cold HBM
+(the copies together are at least twice the 256 MB Infinity Cache).  The K
+timed steps are captured once in a HIP graph and replayed, so the host's
+launch cost does not starve the GPU; HIP events bracket the replay on the
+stream the kernels run on.
+
+One JSON line is printed per workload (by default only the decode gate+up
+GEMV, M=1 K=7168 N=4096, which the headline metric is quoted on).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "W4A16 GEMM effective HBM GB/s (M≤64) and TFLOP/s (M=4096), % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["int4_weight_only_03_amd/csrc/gemv.hip", "int4_weight_only_03_amd/csrc/tile.hip",
+                  "int4_weight_only_03_amd/csrc/w4a16_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter runs, if the kernels are unchanged."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+RIDGE = FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # ~19.7 FLOP per HBM byte
+
+
+def is_hbm_bound(wl) -> bool:
+    """Below the fp32 ridge the kernel is bound by HBM, above it by fp32 math."""
+    return wl.flops() / wl.algorithmic_bytes() < RIDGE
+
+
+def metric_in_gbs(wl) -> bool:
+    """The metric is effective HBM GB/s for M <= 64 and TFLOP/s above."""
+    return wl.M <= 64
+
+
+def gpu_leg(name: str, steps: int, warmup: int):
+    import torch
+    import int4_weight_only_03_amd as pkg
+
+    wl = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    X, W = workloads.make(name)
+    qw, sc = pkg.w4a16_quantize(W)            # the library's own host quantizer
+    B = wl.algorithmic_bytes()
+    copies = 1 if B * 2 > 4 * MALL_BYTES else max(1, -(-2 * MALL_BYTES // B))
+    if name == "tiny":
+        copies = 1                             # cache-resident by nature
+    Xd = torch.from_numpy(X).to(dev)
+    Qd = torch.from_numpy(qw).to(dev)
+    Sd = torch.from_numpy(sc).to(dev)
+    sets = [(Xd.clone(), Qd.clone(), Sd.clone(),
+             torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)) for _ in range(copies)]
+    del Xd, Qd, Sd
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x, q, s, y = sets[i % copies]
+        pkg.w4a16_gemm(x, q, s, y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-launch durations with events around each launch (eager), for the
+    # kernel-time cross-check against rocprofv3
+    n_ev = min(steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [a.elapsed_time(b) for a, b in evs]
+
+    graphed = True
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()                                  # warm replay
+        torch.cuda.synchronize()
+    except Exception as e:                          # capture refused: time eager launches
+        graphed = False
+        print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if graphed:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / steps
+
+    gbs = B / (ms_per_step * 1e-3) / 1e9
+    tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
+    value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
+    if is_hbm_bound(wl):
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": tfs, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tfs / FP32_PEAK_TFLOPS}
+    roof["traffic"] = measured_traffic(name)
+    med = statistics.median(per_launch_ms)
+    extra = {
+        "graph_replay": graphed,
+        "rotation_copies": copies,
+        "algorithmic_bytes": B,
+        "flops": wl.flops(),
+        "per_launch_event_us_median": med * 1e3,
+        "per_launch_event_us_p10": float(np.percentile(per_launch_ms, 10)) * 1e3,
+        "per_launch_event_us_p90": float(np.percentile(per_launch_ms, 90)) * 1e3,
+        "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9,
+        "tflops_at_event_median": wl.flops() / (med * 1e-3) / 1e12,
+        "path": pkg.w4a16_select_path(wl.M, wl.N, wl.K),
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "fp32_frac": tfs / FP32_PEAK_TFLOPS,
+    }
+    y0 = sets[0][3].cpu().numpy()
+    return value, unit, ms_per_step, roof, extra, (X, W, y0)
+
+
+def cpu_leg(name: str, gpu_out, budget_s: float = 12.0):
+    """The oracle, as it stands, timed on the host cores over a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                               # pragma: no cover
+        threadpool_limits = None
+    wl = workloads.WORKLOADS[name]
+    X, W, Y = gpu_out
+    cores = len(os.sched_getaffinity(0))
+    qw, sc = oracle.quantize(W)
+    # sample: all N outputs of up to 8 rows of X (the whole job when M <= 8)
+    rows = min(wl.M, 8)
+    Xs = np.ascontiguousarray(X[:rows])
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        times = []
+        t_end = time.perf_counter() + budget_s
+        Yref = None
+        while time.perf_counter() < t_end or not times:
+            t0 = time.perf_counter()
+            Yref = oracle.gemm(Xs, qw, sc)            # dequant + fp64 product
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 50:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    t = statistics.median(times)
+    # the sample's share of the workload's algorithmic bytes / flops
+    sample_bytes = wl.N * wl.K // 2 + 4 * wl.N * (wl.K // 32) + 4 * rows * wl.K + 4 * rows * wl.N
+    sample_flops = 2 * rows * wl.N * wl.K
+    if metric_in_gbs(wl):
+        value, unit = sample_bytes / t / 1e9, "GB/s"
+    else:
+        value, unit = sample_flops / t / 1e12, "TFLOP/s"
+    T = oracle.abs_gemm(Xs, qw, sc)
+    err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.bound(T)
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of X against all {wl.N} weight rows "
+                      f"(dequant + fp64 product), median of {len(times)} runs, "
+                      f"{t * 1e3:.1f} ms each",
+            "gpu_parity_on_sample_max_err_over_bound": float(err.max())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_gate_up",
+                    help="one of %s, or 'all'" % ", ".join(workloads.ORDER))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    names = workloads.ORDER if args.workload == "all" else [args.workload]
+    for name in names:
+        wl = workloads.WORKLOADS[name]
+        steps = args.steps if wl.M < 1024 else max(5, min(args.steps, 20))
+        print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps}", file=sys.stderr, flush=True)
+        value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup)
+        line = {
+            "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": name, "M": wl.M, "K": wl.K, "N": wl.N, "group": 32,
+                       "note": wl.note, "parallelism": "none (1 GPU)"},
+            "roofline": roof,
+        }
+        line.update(extra)
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_leg(name, out)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

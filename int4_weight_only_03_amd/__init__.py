@@ -1,0 +1,16 @@
+"""MI355X (gfx950) W4A16 group-quantized GEMM: C-ABI library and its Python binding."""
+
+from .binding import (  # noqa: F401
+    GROUP,
+    W4A16_PATH_AUTO,
+    W4A16_PATH_GEMV,
+    W4A16_PATH_TILE,
+    W4A16Error,
+    load,
+    w4a16_abi_version,
+    w4a16_gemm,
+    w4a16_gemm_path,
+    w4a16_quantize,
+    w4a16_select_path,
+    w4a16_status_str,
+)

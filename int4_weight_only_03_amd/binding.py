@@ -1,0 +1,150 @@
+"""Thin ctypes binding of libw4a16.so: argument marshalling only.
+
+Every function keeps the name of the C entry point it calls.  Device buffers
+are PyTorch tensors on a ROCm device (PyTorch provides memory and streams);
+the arithmetic runs in the library's HIP kernels.  There is no fallback: if
+the library cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a16.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a16.h")
+
+GROUP = 32
+W4A16_OK = 0
+W4A16_PATH_AUTO = 0
+W4A16_PATH_GEMV = 1
+W4A16_PATH_TILE = 2
+
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({w4a16_status_str(status)})")
+
+
+_SIGS = {
+    "w4a16_abi_version": ([], ctypes.c_int),
+    "w4a16_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "w4a16_quantize": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                        ctypes.c_int64, ctypes.c_int32], ctypes.c_int),
+    "w4a16_gemm": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                    ctypes.c_void_p], ctypes.c_int),
+    "w4a16_gemm_path": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                         ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_select_path": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/w4a16.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+
+
+def load(path: str | None = None):
+    """Load the library (building it first only if no build exists)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def w4a16_abi_version() -> int:
+    return load().w4a16_abi_version()
+
+
+def w4a16_status_str(status: int) -> str:
+    return load().w4a16_status_str(int(status)).decode()
+
+
+def w4a16_select_path(M: int, N: int, K: int) -> int:
+    return load().w4a16_select_path(M, N, K)
+
+
+def w4a16_quantize(W: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Host quantizer: W fp32 [N][K] -> (qweight int32 [N][K/8], scales fp32 [N][K/32])."""
+    W = np.ascontiguousarray(W)
+    if W.dtype != np.float32 or W.ndim != 2:
+        raise TypeError("W must be a 2-D float32 array")
+    N, K = W.shape
+    qw = np.empty((N, max(K // 8, 0)), dtype=np.int32)
+    sc = np.empty((N, max(K // GROUP, 0)), dtype=np.float32)
+    st = load().w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, N, K, GROUP)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_quantize")
+    return qw, sc
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a tensor on a ROCm device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def w4a16_gemm_path(X, qweight, scales, Y=None, path: int = W4A16_PATH_AUTO, stream=None):
+    """Y = X . dequant(qweight, scales)^T on the device, with the kernel path forced."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    if X.dim() != 2 or qweight.dim() != 2 or scales.dim() != 2:
+        raise ValueError("X, qweight and scales must be 2-D")
+    M, K = X.shape
+    N = qweight.shape[0]
+    if K % 8 or qweight.shape[1] != K // 8 or tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError(f"shapes disagree: X {tuple(X.shape)}, qweight "
+                         f"{tuple(qweight.shape)}, scales {tuple(scales.shape)}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    st = load().w4a16_gemm_path(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                                Y.data_ptr(), M, N, K, GROUP, int(path),
+                                _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_path")
+    return Y
+
+
+def w4a16_gemm(X, qweight, scales, Y=None, stream=None):
+    """Y = X . dequant(qweight, scales)^T on the device (path chosen by the library)."""
+    return w4a16_gemm_path(X, qweight, scales, Y, W4A16_PATH_AUTO, stream)

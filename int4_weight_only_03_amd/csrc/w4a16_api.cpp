@@ -1,0 +1,131 @@
+// C-ABI layer: argument validation, path dispatch, host quantizer, status text.
+//
+// The quantizer follows the pages' quantize_w4a16 ("The Quiet Commit: How a
+// Single Documentation Edit Marks the Completion of a Major Engineering
+// Milestone", section "The INT4 Milestone": symmetric, group 32, 8 nibbles
+// per int32 along K, value = nibble - 8).  The pages do not print the scale or
+// rounding rule; this file uses scale = max|w|/7 and q = clamp(rint(w/scale),
+// -8, 7), each division an IEEE fp32 true division rounded to nearest even.
+// It is compiled without FMA contraction or fast-math so that it is bit-exact
+// with any IEEE implementation of the same steps.
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int validate_gemm(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                  int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!X || !qweight || !scales || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(qweight, 16) || !aligned(scales, 4) || !aligned(Y, 4))
+    return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(M) * size_t(K) * 4, bq = size_t(N) * size_t(K) / 2,
+               bs = size_t(N) * size_t(K / W4A16_GROUP) * 4, by = size_t(M) * size_t(N) * 4;
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, qweight, bq) || overlaps(Y, by, scales, bs))
+    return W4A16_ERR_ARG;
+  return W4A16_OK;
+}
+
+int select_path(int64_t M) { return M <= w4a16::kGemvMaxM ? W4A16_PATH_GEMV : W4A16_PATH_TILE; }
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char *w4a16_status_str(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_ARG: return "invalid argument";
+    case W4A16_ERR_SHAPE: return "unsupported shape (K must be a multiple of 32; extents within limits)";
+    case W4A16_ERR_ALIGN: return "misaligned pointer (X, qweight: 16 bytes; scales, Y: 4 bytes)";
+    case W4A16_ERR_NONFINITE: return "non-finite weight";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return select_path(M);
+}
+
+int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                    int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, void *stream) {
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_TILE)
+    return W4A16_ERR_ARG;
+  int st = validate_gemm(X, qweight, scales, Y, M, N, K, group);
+  if (st != W4A16_OK || M == 0 || N == 0) return st;
+  if (path == W4A16_PATH_AUTO) path = select_path(M);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (path == W4A16_PATH_GEMV)
+                     ? w4a16::launch_gemv(X, qweight, scales, Y, int(M), int(N), int(K), s)
+                     : w4a16::launch_tile(X, qweight, scales, Y, int(M), int(N), int(K), s);
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, float *Y, int64_t M,
+               int64_t N, int64_t K, int32_t group, void *stream) {
+  return w4a16_gemm_path(X, qweight, scales, Y, M, N, K, group, W4A16_PATH_AUTO, stream);
+}
+
+int w4a16_quantize(const float *W, int32_t *qweight, float *scales, int64_t N, int64_t K,
+                   int32_t group) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (N == 0) return W4A16_OK;
+  if (!W || !qweight || !scales) return W4A16_ERR_ARG;
+  const size_t total = size_t(N) * size_t(K);
+  for (size_t i = 0; i < total; ++i)
+    if (!std::isfinite(W[i])) return W4A16_ERR_NONFINITE;
+
+  const int64_t G = K / W4A16_GROUP;
+  for (int64_t n = 0; n < N; ++n) {
+    const float *wrow = W + size_t(n) * size_t(K);
+    uint32_t *qrow = reinterpret_cast<uint32_t *>(qweight) + size_t(n) * size_t(K / 8);
+    for (int64_t g = 0; g < G; ++g) {
+      const float *w = wrow + g * W4A16_GROUP;
+      float amax = 0.0f;
+      for (int i = 0; i < W4A16_GROUP; ++i) amax = std::fmax(amax, std::fabs(w[i]));
+      volatile float seven = 7.0f;  // keep a true division, never a reciprocal multiply
+      const float scale = amax / seven;
+      scales[size_t(n) * size_t(G) + size_t(g)] = scale;
+      uint32_t words[W4A16_GROUP / 8] = {0, 0, 0, 0};
+      for (int i = 0; i < W4A16_GROUP; ++i) {
+        float q = 0.0f;
+        if (scale != 0.0f) {
+          const float ratio = w[i] / scale;   // fp32 true division
+          q = std::nearbyint(ratio);          // default mode: nearest, ties to even
+          if (q < -8.0f) q = -8.0f;
+          if (q > 7.0f) q = 7.0f;
+        }
+        const uint32_t nib = uint32_t(int(q) + 8);
+        words[i / 8] |= nib << (4 * (i % 8));
+      }
+      std::memcpy(qrow + g * (W4A16_GROUP / 8), words, sizeof(words));
+    }
+  }
+  return W4A16_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// Internal interface between the C-ABI layer (w4a16_api.cpp) and the kernel
+// translation units.  Arguments reaching these launchers are already
+// validated: pointers non-NULL and aligned, 0 < M, N, 0 < K, K % 32 == 0,
+// extents within the W4A16_MAX_* limits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+constexpr int kGroup = 32;
+
+// Decode/verify path: dequant-on-the-fly GEMV with activations held in VGPRs.
+hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                       int M, int N, int K, hipStream_t stream);
+
+// Tiled path: fp32 MFMA (32x32x2) on weight tiles dequantized into registers.
+hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                       int M, int N, int K, hipStream_t stream);
+
+// Largest M the GEMV path is chosen for by default.
+constexpr int kGemvMaxM = 4;
+
+}  // namespace w4a16

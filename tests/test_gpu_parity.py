@@ -1,0 +1,174 @@
+"""GPU parity of the HIP paths against the CPU oracle, through the C ABI.
+
+Inputs are seeded synthetic draws (workloads), quantized by the oracle, so no
+input or expected value comes from the HIP path.  Every output is checked
+against |Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6 (fp64 oracle), except
+at the prefill size, where sampled entries are checked one dot product at a
+time.  Integer-valued inputs with a common power-of-two scale must match
+exactly, since any fp32 summation order is exact on them.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_only_03_amd import binding  # noqa: E402
+
+PATHS = {"gemv": binding.W4A16_PATH_GEMV, "tile": binding.W4A16_PATH_TILE}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run(X, qw, sc, path, dev):
+    Xd, Qd, Sd = to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev)
+    Y = binding.w4a16_gemm_path(Xd, Qd, Sd, path=path)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def check(Y, X, qw, sc, what):
+    v = oracle.compare(Y, X, qw, sc)
+    say(f"{what}: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], (what, v)
+    return v
+
+
+SHAPES = [
+    # (M, N, K): ragged M, N not a tile multiple, K from one group to K2.6 width
+    (1, 1, 32), (1, 33, 96), (1, 257, 224), (1, 100, 7168), (1, 64, 16384 + 32),
+    (2, 31, 64), (3, 65, 256), (4, 128, 512), (5, 17, 32), (17, 70, 160),
+    (63, 33, 96), (64, 64, 2048), (65, 129, 224), (127, 95, 128), (130, 200, 320),
+    (300, 260, 256),
+]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_shapes(dev, path, M, N, K):
+    say(f"shape M={M} N={N} K={K} path={path}")
+    X, W = workloads.random_case(M, N, K, seed=M * 1000003 + N * 101 + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, PATHS[path], dev), X, qw, sc, f"{path} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_gate_up", "decode_down", "verify_tree"])
+def test_named_workloads_every_output(dev, name):
+    say(f"workload {name}")
+    X, W = workloads.make(name)
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, binding.W4A16_PATH_AUTO, dev)
+    check(Y, X, qw, sc, name)
+    # negative control: the unquantized product lies outside the bound
+    plain = X.astype(np.float64) @ W.astype(np.float64).T
+    assert not oracle.compare(plain, X, qw, sc)["ok"]
+
+
+def test_prefill_sampled(dev):
+    say("workload prefill (sampled)")
+    X, W = workloads.make("prefill")
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, binding.W4A16_PATH_AUTO, dev)
+    assert np.all(np.isfinite(Y))
+    rng = np.random.default_rng(123)
+    M, N = Y.shape
+    rows = np.concatenate([rng.integers(0, M, 1500), [0, M - 1, 0, M - 1]])
+    cols = np.concatenate([rng.integers(0, N, 1500), [0, N - 1, N - 1, 0]])
+    v = oracle.compare_entries(Y, X, qw, sc, rows, cols)
+    say(f"prefill sampled: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("M,N,K", [(1, 300, 7168), (3, 50, 224), (64, 96, 7168), (200, 130, 512)])
+def test_integer_inputs_exact(dev, path, M, N, K):
+    say(f"integer exact M={M} N={N} K={K} path={path}")
+    X, nib = workloads.integer_case(M, N, K, seed=K + N)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), dtype=np.float32)
+    Y = run(X, qw, sc, PATHS[path], dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_one_hot_weights(dev, path):
+    # one weight of +-1*s per row at varying k; everything else exactly zero
+    rng = np.random.default_rng(2)
+    M, N, K = 3, 40, 7168
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    nib = np.full((N, K), 8, np.uint8)
+    ks = rng.integers(0, K, N)
+    nib[np.arange(N), ks] = np.where(rng.random(N) < 0.5, 9, 7)
+    qw = oracle.pack(nib)
+    sc = rng.uniform(0.5, 2.0, (N, K // 32)).astype(np.float32)
+    Y = run(X, qw, sc, PATHS[path], dev)
+    check(Y, X, qw, sc, f"one-hot {path}")
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_deterministic_and_scale_equivariant(dev, path):
+    X, W = workloads.random_case(5, 300, 2048, seed=77)
+    qw, sc = oracle.quantize(W)
+    a = run(X, qw, sc, PATHS[path], dev)
+    b = run(X, qw, sc, PATHS[path], dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = run((X * np.float32(8.0)).astype(np.float32), qw, sc, PATHS[path], dev)
+    assert np.array_equal(c, a * np.float32(8.0))
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_no_write_outside_y(dev, path):
+    M, N, K = 7, 45, 96
+    X, W = workloads.random_case(M, N, K, seed=3)
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y, PATHS[path])
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    check(Y.cpu().numpy(), X, qw, sc, f"guarded {path}")
+
+
+def test_empty_is_noop(dev):
+    X = torch.zeros((0, 64), device=dev)
+    Q = torch.zeros((5, 8), dtype=torch.int32, device=dev)
+    S = torch.zeros((5, 2), device=dev)
+    Y = binding.w4a16_gemm(X, Q, S)
+    assert tuple(Y.shape) == (0, 5)
+
+
+def test_library_quantize_feeds_gpu(dev):
+    X, W = workloads.make("tiny")
+    qw, sc = binding.w4a16_quantize(W)
+    Y = run(X, qw, sc, binding.W4A16_PATH_AUTO, dev)
+    check(Y, X, *oracle.quantize(W), "tiny via library quantize")
+
+
+def test_native_library_is_loaded(dev):
+    path = os.path.realpath(binding.LIB_PATH)
+    maps = open("/proc/self/maps").read()
+    assert path in maps

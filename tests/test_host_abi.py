@@ -1,0 +1,150 @@
+"""Host-side tests of the C-ABI library (no GPU is touched).
+
+* the library loads and exports every function include/w4a16.h declares;
+* the host quantizer is bit-exact with the oracle (one correct result);
+* argument errors come back synchronously with the documented codes, before
+  any launch: these calls use fake device addresses that are never dereferenced.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from int4_weight_only_03_amd import binding
+
+OK, ARG, SHAPE, ALIGN, NONFINITE, HIP = 0, 1, 2, 3, 4, 5
+
+
+def test_exports_every_declared_symbol(lib):
+    names = binding.header_functions()
+    assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
+            "w4a16_abi_version", "w4a16_select_path"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.w4a16_abi_version() == 1
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in (OK, ARG, SHAPE, ALIGN, NONFINITE, HIP):
+        text = binding.w4a16_status_str(code)
+        assert text and text not in seen
+        seen.add(text)
+    assert binding.w4a16_status_str(99) == "unknown status"
+
+
+def test_select_path(lib):
+    assert binding.w4a16_select_path(1, 4096, 7168) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(4, 4096, 7168) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(5, 4096, 7168) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE
+
+
+# ------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("name", ["tiny", "decode_down", "decode_gate_up"])
+def test_quantize_bit_exact_with_oracle(lib, name):
+    W = workloads.make_w(name)
+    qa, sa = binding.w4a16_quantize(W)
+    qb, sb = oracle.quantize(W)
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    assert np.array_equal(qa, qb)
+
+
+def test_quantize_edge_groups(lib):
+    rng = np.random.default_rng(17)
+    W = (0.02 * rng.standard_normal((12, 256))).astype(np.float32)
+    W[0, :32] = 0.0                                        # all-zero group
+    W[1, 32:64] = -0.0                                     # negative zeros
+    W[2, 64:96] = np.float32(2.0 ** -149)                  # scale underflows to 0
+    W[3, :32] = np.ldexp(rng.standard_normal(32), -140).astype(np.float32)  # subnormal scale
+    W[4, :32] = np.arange(32, dtype=np.float32) - 16.0     # 2.5-style ties at scale 16/7
+    W[5, :32] = np.float32(3.0e38) * np.sign(rng.standard_normal(32)).astype(np.float32)
+    W[6, :8] = [7, 3.5, 2.5, -2.5, 0.5, 1.5, -0.5, -7]     # exact ties, scale 1
+    W[7] = np.float32(1e-3) * np.sign(rng.standard_normal(256)).astype(np.float32)
+    qa, sa = binding.w4a16_quantize(W)
+    qb, sb = oracle.quantize(W)
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    assert np.array_equal(qa, qb)
+
+
+def test_quantize_errors_leave_outputs_untouched(lib):
+    W = np.zeros((2, 64), np.float32)
+    W[1, 40] = np.nan
+    qw = np.full((2, 8), 7, np.int32)
+    sc = np.full((2, 2), 5.0, np.float32)
+    st = lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, 2, 64, 32)
+    assert st == NONFINITE
+    assert np.all(qw == 7) and np.all(sc == 5.0)
+    W[1, 40] = -np.inf
+    assert lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, 2, 64, 32) == NONFINITE
+    W[1, 40] = 0.0
+    assert lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, 2, 48, 32) == SHAPE
+    assert lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, 2, 64, 16) == ARG
+    assert lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, -1, 64, 32) == ARG
+    assert lib.w4a16_quantize(W.ctypes.data, qw.ctypes.data, sc.ctypes.data, 2, 0, 32) == ARG
+    assert lib.w4a16_quantize(None, qw.ctypes.data, sc.ctypes.data, 2, 64, 32) == ARG
+    assert lib.w4a16_quantize(None, None, None, 0, 64, 32) == OK
+    assert np.all(qw == 7) and np.all(sc == 5.0)
+    with pytest.raises(binding.W4A16Error):
+        binding.w4a16_quantize(np.zeros((1, 40), np.float32))
+
+
+# ------------------------------------------------------------------ gemm argument errors
+
+def _call(lib, X, Q, S, Y, M, N, K, group=32, path=None):
+    if path is None:
+        return lib.w4a16_gemm(X, Q, S, Y, M, N, K, group, None)
+    return lib.w4a16_gemm_path(X, Q, S, Y, M, N, K, group, path, None)
+
+
+BASE = 1 << 40  # fake device addresses; validation never dereferences them
+X_, Q_, S_, Y_ = BASE, BASE + (1 << 32), BASE + (2 << 32), BASE + (3 << 32)
+
+
+def test_gemm_rejects_bad_arguments_synchronously(lib):
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 64, group=16) == ARG
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 0) == ARG
+    assert _call(lib, X_, Q_, S_, Y_, -1, 8, 64) == ARG
+    assert _call(lib, X_, Q_, S_, Y_, 1, -8, 64) == ARG
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 48) == SHAPE
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 100) == SHAPE
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, (1 << 28) + 32) == SHAPE
+    assert _call(lib, X_, Q_, S_, Y_, 1 << 31, 8, 64) == SHAPE
+    assert _call(lib, None, Q_, S_, Y_, 1, 8, 64) == ARG
+    assert _call(lib, X_, None, S_, Y_, 1, 8, 64) == ARG
+    assert _call(lib, X_, Q_, None, Y_, 1, 8, 64) == ARG
+    assert _call(lib, X_, Q_, S_, None, 1, 8, 64) == ARG
+    assert _call(lib, X_ + 4, Q_, S_, Y_, 1, 8, 64) == ALIGN
+    assert _call(lib, X_, Q_ + 8, S_, Y_, 1, 8, 64) == ALIGN
+    assert _call(lib, X_, Q_, S_ + 2, Y_, 1, 8, 64) == ALIGN
+    assert _call(lib, X_, Q_, S_, Y_ + 1, 1, 8, 64) == ALIGN
+    assert _call(lib, X_, Q_, S_, X_ + 64, 1, 8, 64) == ARG        # Y overlaps X
+    assert _call(lib, X_, Q_, S_, Q_ + 16, 1, 8, 64) == ARG        # Y overlaps qweight
+    assert _call(lib, X_, Q_, S_, S_, 1, 8, 64) == ARG             # Y overlaps scales
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 64, path=3) == ARG
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, 64, path=-1) == ARG
+
+
+def test_gemm_empty_is_a_noop(lib):
+    # M == 0 or N == 0: OK without touching the GPU (no device exists here)
+    assert _call(lib, None, None, None, None, 0, 8, 64) == OK
+    assert _call(lib, None, None, None, None, 3, 0, 64) == OK
+    assert _call(lib, None, None, None, None, 0, 0, 32, path=2) == OK
+    # ...but K is still validated
+    assert _call(lib, None, None, None, None, 0, 8, 40) == SHAPE
+
+
+def test_binding_refuses_host_tensors(lib):
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(1, 64)
+    with pytest.raises(TypeError):
+        binding.w4a16_gemm(X, torch.zeros(8, 8, dtype=torch.int32), torch.zeros(8, 2))
+
+
+def test_header_names_match_binding():
+    assert set(binding.header_functions()) == set(binding._SIGS)
+    assert isinstance(ctypes.sizeof(ctypes.c_void_p), int)
