@@ -9,24 +9,28 @@
 // Success: A Single Line That Speaks Volumes", section "Assumptions Embedded
 // in the Code"), so the inner loop is counted in VALU operations per weight.
 //
-// Mapping (gfx950, wave64):
-//  * A thread owns one group column g (32 consecutive k) and keeps the 32
-//    activations of that group in VGPRs for every W row it visits, so the
-//    activation vector is read once per thread, not once per weight.
-//  * One 16-byte load (global_load_dwordx4) brings exactly one group of one W
-//    row: 4 words = 32 nibbles.  A row slot of TPS = G threads reads one W row
-//    as one contiguous run; consecutive slots read consecutive rows, so a wave
-//    reads contiguous memory.  Each thread issues all RB row loads (and their
-//    scales) before it touches any of them.
+// Arithmetic (both kernels below):
+//  * One 16-byte load brings exactly one group of one W row: 4 words = 32
+//    nibbles.  A compute thread owns one group column g and keeps its 32
+//    activations in VGPRs for every W row it visits.
 //  * Nibbles become signed bytes 16*(q-8) with one or two bit operations per
 //    word (mask the high nibbles, or shift-and-mask the low nibbles, then flip
 //    bit 7: v_bitop3); each byte converts to fp32 exactly (v_cvt_f32_i32 with a
 //    sign-extended SDWA byte select) and meets x in one FMA; the group sum is
-//    two fp32 chains (even and odd k), then multiplied by 1/16 exactly.
-//  * The group's scale multiplies the 32-term group sum (scale-after-sum);
-//    the per-thread partials of a row are summed across the slot in LDS and
-//    by a shuffle tree within aligned lane teams.  No atomics: results are
+//    two fp32 chains (even and odd k), multiplied by 1/16 exactly, and the
+//    group's scale multiplies that sum (scale after the 32-term sum).
+//  * No atomics: every output is summed in a fixed order, so results are
 //    deterministic run to run.
+//
+// Fast kernel (M <= 2): wave-specialised.  The first kLoaders threads of a
+// block stage the activation rows in LDS while every other wave issues all
+// of its weight and scale loads straight away (straight-line code, clamped
+// row indices, no branches between loads), so the weights stream from the
+// first cycle and no wave's in-order load counter ties activations to
+// weights.  Partial sums are reduced with DPP row shifts and row broadcasts
+// inside aligned lane segments (no LDS round trip), and one LDS pass adds the
+// few segment sums of a row.  Blocks are sized so that the grid is about one
+// block per compute unit.
 
 #include "w4a16_internal.h"
 
@@ -35,8 +39,14 @@
 namespace w4a16 {
 namespace {
 
-// Block size cap: 8 waves per block leaves up to 256 VGPRs per lane.
-constexpr int kMaxBlock = 512;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint4 *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float load_stream4(const float *p) { return __builtin_nontemporal_load(p); }
 
 // sum over the group of x_k * 16*(q_k - 8): the 16*(q-8) are exact signed
 // bytes, each met by one fp32 FMA (one rounding per term).
@@ -58,9 +68,206 @@ __device__ __forceinline__ float group_dot16(const float (&x)[32], uint4 w) {
   return a0 + a1;
 }
 
-// One block covers S*RB consecutive W rows.  Thread t: slot = t / TPS, column
-// c = t % TPS; slot s handles rows rowbase + s + i*S (i < RB) and groups
-// c, c+TPS, ... .  T = lanes per reduction team (power of two <= 64).
+// Sum over aligned segments of Z lanes (Z = 16, 32 or 64); the last lane of
+// each segment receives the segment total.  Row shifts 1, 2, 4, 8 accumulate
+// each 16-lane row into its lane 15 (lanes past the row edge read 0),
+// row_bcast:15 adds lane 15 of rows 0 and 2 into rows 1 and 3, and
+// row_bcast:31 adds lane 31 into rows 2 and 3.
+template <int Z>
+__device__ __forceinline__ float segment_sum(float v) {
+  static_assert(Z == 16 || Z == 32 || Z == 64, "segment of 16, 32 or 64 lanes");
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+  if constexpr (Z >= 32)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  if constexpr (Z >= 64)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+constexpr int kFastMaxBlock = 768;  // 12 waves: up to 170 VGPRs per lane
+constexpr int kLoaders = 128;       // activation-staging threads per block (fast kernel)
+constexpr int kXChunk = 16;         // float4 each staging thread moves (32 KB per block)
+constexpr int kFastMaxLds = 64 * 1024;
+
+// Fast kernel (M = MT).  Thread t < kLoaders stages the MT rows of X in LDS;
+// thread kLoaders + s*G + c (c < G, s < S) is compute thread (slot s, group
+// c) for rows rowbase + s + i*S, i < RB.  Z (16, 32 or 64) divides G, so
+// segments of Z compute lanes never straddle a slot.
+template <int MT, int RB, int Z>
+__global__ void __launch_bounds__(kFastMaxBlock)
+gemv_ws(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
+        float *__restrict__ Y, int M, int N, int G, int S) {
+  extern __shared__ __align__(16) float lds[];
+  const long K = long(G) * kGroup;
+  const int rowx4 = G * 8;            // float4 per activation row
+  const int nx4 = MT * rowx4;         // float4 staged (all M = MT rows)
+  float *xs = lds;                    // [MT][K] activations, then one pad float4
+  float *part = lds + 4 * (nx4 + 1);  // [segments][MT*RB] segment partial sums
+  const int t = threadIdx.x;
+  const bool loader = t < kLoaders;
+  const int c = t - kLoaders;
+  const int slot0 = loader ? 0 : c / G;
+  const bool active = !loader && slot0 < S;
+  const int slot = active ? slot0 : 0;
+  const int g = active ? c - slot0 * G : 0;
+  const long rowbase = long(blockIdx.x) * S * RB;
+  float acc[MT][RB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[m][i] = 0.0f;
+  uint4 w[RB];
+  float s[RB];
+  if (loader) {  // one straight-line pass: nx4 <= kLoaders * kXChunk
+    float4 v[kXChunk];
+#pragma unroll
+    for (int u = 0; u < kXChunk; ++u) {
+      const int k = std::min(t + u * kLoaders, nx4 - 1);
+      const int mr = (MT > 1 && k >= rowx4) ? 1 : 0;
+      v[u] = reinterpret_cast<const float4 *>(X + mr * K)[k - mr * rowx4];
+    }
+    // every staging load is issued before the first store waits on one: the
+    // empty asm consumes all loaded values at once
+#pragma unroll
+    for (int u = 0; u < kXChunk; ++u) asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
+#pragma unroll
+    for (int u = 0; u < kXChunk; ++u)  // out-of-range threads write the pad slot
+      reinterpret_cast<float4 *>(xs)[std::min(t + u * kLoaders, nx4)] = v[u];
+  } else {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {  // clamped rows: no branch between loads
+      const long n = std::min(rowbase + slot + long(i) * S, long(N) - 1);
+      w[i] = load_stream16(qw + n * G + g);
+      s[i] = load_stream4(sc + n * G + g);
+    }
+  }
+  __syncthreads();
+  if (!loader) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float x[32];
+      const float4 *xp = reinterpret_cast<const float4 *>(xs + m * K + long(g) * kGroup);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float4 f = xp[v];
+        x[4 * v + 0] = f.x;
+        x[4 * v + 1] = f.y;
+        x[4 * v + 2] = f.z;
+        x[4 * v + 3] = f.w;
+      }
+      // scale * (group sum / 16): the power-of-two 1/16 is exact
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        acc[m][i] = active ? s[i] * (group_dot16(x, w[i]) * 0.0625f) : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[m][i] = segment_sum<Z>(acc[m][i]);
+    if ((c & (Z - 1)) == Z - 1) {
+      const int seg = c / Z;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < RB; ++i) part[seg * (MT * RB) + m * RB + i] = acc[m][i];
+    }
+  }
+  __syncthreads();
+  const int sps = G / Z;  // segments per slot
+  for (int o = t; o < S * MT * RB; o += blockDim.x) {
+    const int sl = o / (MT * RB);
+    const int r = o - sl * (MT * RB);
+    const int m = r / RB;
+    const int i = r - m * RB;
+    float v = 0.0f;
+    for (int k = 0; k < sps; ++k) v += part[(sl * sps + k) * (MT * RB) + m * RB + i];
+    const long n = rowbase + sl + long(i) * S;
+    if (m < M && n < N) Y[long(m) * N + n] = v;
+  }
+}
+
+struct FastPlan {
+  int MT, RB, S, Z, BS, blocks;
+  size_t lds;
+};
+
+// Fast kernel plan: about one block per compute unit (256 on MI355X).
+bool plan_fast(int M, int N, int G, FastPlan &p) {
+  if (M > 2) return false;
+  p.MT = M;  // the fast kernel stages all M rows at once
+  p.Z = 1;
+  while (p.Z < 64 && G % (2 * p.Z) == 0) p.Z *= 2;
+  if (p.Z < 16) return false;  // segments of 16, 32 or 64 lanes only
+  const int s_max = (kFastMaxBlock - kLoaders) / G;
+  if (s_max < 1) return false;
+  const long rows_per_block = std::max(1L, (long(N) + 255) / 256);
+  const int prefs[4] = {4, 8, 2, 1};
+  p.RB = 0;
+  for (int rb : prefs) {
+    if (rb * p.MT > 8) continue;  // MT*RB <= 8 partial sums keeps the kernel spill-free
+    const long s = (rows_per_block + rb - 1) / rb;
+    if (s <= s_max) {
+      p.RB = rb;
+      p.S = int(s);
+      break;
+    }
+  }
+  if (p.RB == 0) {  // very tall W: widest blocks, more of them
+    p.RB = 8 / p.MT;
+    p.S = s_max;
+  }
+  if (long(p.MT) * G * 8 > long(kLoaders) * kXChunk) return false;  // one staging pass
+  p.BS = ((kLoaders + p.S * G + 63) / 64) * 64;
+  p.blocks = int((long(N) + long(p.S) * p.RB - 1) / (long(p.S) * p.RB));
+  const size_t segs = size_t(p.BS - kLoaders) / p.Z + 1;
+  p.lds = 16 * (size_t(p.MT) * G * 8 + 1) + segs * p.MT * p.RB * sizeof(float);
+  return p.lds <= size_t(kFastMaxLds);
+}
+
+template <int MT, int RB, int Z>
+hipError_t run_fast(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
+                    float *Y, int M, int N, int G, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_ws<MT, RB, Z>), dim3(p.blocks), dim3(p.BS), p.lds, stream, X,
+                     reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G, p.S);
+  return hipGetLastError();
+}
+
+template <int Z>
+hipError_t dispatch_fast_z(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
+                           float *Y, int M, int N, int G, hipStream_t stream) {
+  switch (p.MT * 16 + p.RB) {
+    case 1 * 16 + 8: return run_fast<1, 8, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 4: return run_fast<1, 4, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 2: return run_fast<1, 2, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 1: return run_fast<1, 1, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 4: return run_fast<2, 4, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 2: return run_fast<2, 2, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 1: return run_fast<2, 1, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t dispatch_fast(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
+                         float *Y, int M, int N, int G, hipStream_t stream) {
+  switch (p.Z) {
+    case 64: return dispatch_fast_z<64>(p, X, qw, sc, Y, M, N, G, stream);
+    case 32: return dispatch_fast_z<32>(p, X, qw, sc, Y, M, N, G, stream);
+    case 16: return dispatch_fast_z<16>(p, X, qw, sc, Y, M, N, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// General kernel (any M, any K): each thread loads its activations straight
+// from memory.  One block covers S*RB consecutive W rows.  Thread t: slot =
+// t / TPS, column c = t % TPS; slot s handles rows rowbase + s + i*S (i < RB)
+// and groups c, c+TPS, ... .  T = lanes per reduction team (power of two <= 64).
+
+constexpr int kMaxBlock = 512;  // 8 waves per block leaves up to 256 VGPRs per lane
+
 template <int MT, int RB>
 __global__ void __launch_bounds__(kMaxBlock)
 gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
@@ -88,34 +295,24 @@ gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
         uint4 w[RB];
         float s[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const long n = rowbase + slot + long(i) * S;
-          if (n < N) {
-            w[i] = qw[n * G + g];
-            s[i] = sc[n * G + g];
-          } else {
-            w[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-            s[i] = 0.0f;
-          }
+        for (int i = 0; i < RB; ++i) {  // clamped rows: no branch between loads
+          const long n = std::min(rowbase + slot + long(i) * S, long(N) - 1);
+          w[i] = load_stream16(qw + n * G + g);
+          s[i] = load_stream4(sc + n * G + g);
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           float x[32];
-          if (m0 + m < M) {
-            const float4 *xp = reinterpret_cast<const float4 *>(X + long(m0 + m) * K + long(g) * kGroup);
+          const int row = std::min(m0 + m, M - 1);  // rows past M are computed and dropped
+          const float4 *xp = reinterpret_cast<const float4 *>(X + long(row) * K + long(g) * kGroup);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              const float4 f = xp[v];
-              x[4 * v + 0] = f.x;
-              x[4 * v + 1] = f.y;
-              x[4 * v + 2] = f.z;
-              x[4 * v + 3] = f.w;
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 32; ++v) x[v] = 0.0f;
+          for (int v = 0; v < 8; ++v) {
+            const float4 f = xp[v];
+            x[4 * v + 0] = f.x;
+            x[4 * v + 1] = f.y;
+            x[4 * v + 2] = f.z;
+            x[4 * v + 3] = f.w;
           }
-          // scale * (group sum / 16): the power-of-two 1/16 is exact
 #pragma unroll
           for (int i = 0; i < RB; ++i)
             acc[m][i] = fmaf(s[i], group_dot16(x, w[i]) * 0.0625f, acc[m][i]);
@@ -221,6 +418,8 @@ hipError_t dispatch(const GemvPlan &p, const float *X, const int32_t *qw, const 
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream) {
   const int G = K / kGroup;
+  FastPlan fp;
+  if (plan_fast(M, N, G, fp)) return dispatch_fast(fp, X, qweight, scales, Y, M, N, G, stream);
   return dispatch(plan_gemv(M, N, G), X, qweight, scales, Y, M, N, G, stream);
 }
 
