@@ -217,6 +217,19 @@ def cpu_leg(name: str, gpu_out, budget_s: float = 12.0):
             "gpu_parity_on_sample_max_err_over_bound": float(err.max())}
 
 
+def copy_probe(nbytes: int, reps: int = 20) -> None:
+    """Plain device copy of a known size, for calibrating HBM byte counters."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,7 +238,12 @@ def main():
     ap.add_argument("--workload", default="decode_gate_up",
                     help="one of %s, or 'all'" % ", ".join(workloads.ORDER))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)

@@ -202,8 +202,9 @@ hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scal
   const long big_tiles = long((M + 127) / 128) * ((N + 127) / 128);
   if (M > 64 && big_tiles >= 512)
     return run<2, 2, 2, 2, 1>(X, qweight, scales, Y, M, N, G, stream);
-  if (M > 32)  // skinny: 64 x 32 tiles, groups split over 8 waves
-    return run<2, 1, 1, 1, 8>(X, qweight, scales, Y, M, N, G, stream);
+  // Otherwise 32 x 32 block tiles with the groups split over 8 waves: the
+  // smallest tile gives the most blocks, so skinny shapes still fill all
+  // compute units (M=64, N=4096: 256 blocks).
   return run<1, 1, 1, 1, 8>(X, qweight, scales, Y, M, N, G, stream);
 }
 
