@@ -36,10 +36,13 @@ import workloads  # noqa: E402
 METRIC = "W4A16 GEMM effective HBM GB/s (M≤64) and TFLOP/s (M=4096), % of roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
+FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["int4_weight_only_03_amd/csrc/gemv.hip", "int4_weight_only_03_amd/csrc/tile.hip",
+                  "int4_weight_only_03_amd/csrc/split.hip",
                   "int4_weight_only_03_amd/csrc/w4a16_api.cpp"]
+PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3}
 
 
 def kernel_source_hash() -> str:
@@ -50,24 +53,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter runs, if the kernels are unchanged."""
+def measured_traffic(workload: str, path: str):
+    """HBM bytes per call from the committed counter runs, if the kernels are unchanged."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    entry = rec.get("workloads", {}).get(workload)
+    key = workload if path == "auto" else f"{workload}/{path}"
+    entry = rec.get("workloads", {}).get(key)
     return None if entry is None else entry.get("bytes_per_launch")
-
-
-RIDGE = FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # ~19.7 FLOP per HBM byte
-
-
-def is_hbm_bound(wl) -> bool:
-    """Below the fp32 ridge the kernel is bound by HBM, above it by fp32 math."""
-    return wl.flops() / wl.algorithmic_bytes() < RIDGE
 
 
 def metric_in_gbs(wl) -> bool:
@@ -75,7 +71,7 @@ def metric_in_gbs(wl) -> bool:
     return wl.M <= 64
 
 
-def gpu_leg(name: str, steps: int, warmup: int):
+def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     import torch
     import int4_weight_only_03_amd as pkg
 
@@ -94,10 +90,19 @@ def gpu_leg(name: str, steps: int, warmup: int):
              torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)) for _ in range(copies)]
     del Xd, Qd, Sd
     stream = torch.cuda.current_stream(dev)
+    code = PATH_NAMES[path]
+    if code == pkg.W4A16_PATH_SPLIT:
+        # one caller-owned workspace, reused by every (stream-ordered) step
+        ws = torch.empty(pkg.w4a16_split_workspace_bytes(wl.M, wl.N, wl.K), dtype=torch.uint8,
+                         device=dev)
 
-    def step(i):
-        x, q, s, y = sets[i % copies]
-        pkg.w4a16_gemm(x, q, s, y)
+        def step(i):
+            x, q, s, y = sets[i % copies]
+            pkg.w4a16_gemm_split(x, q, s, y, workspace=ws)
+    else:
+        def step(i):
+            x, q, s, y = sets[i % copies]
+            pkg.w4a16_gemm_path(x, q, s, y, path=code)
 
     for i in range(warmup):
         step(i)
@@ -144,13 +149,16 @@ def gpu_leg(name: str, steps: int, warmup: int):
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
     value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
-    if is_hbm_bound(wl):
+    split = code == pkg.W4A16_PATH_SPLIT
+    # the split path issues fp16 matrix instructions: its compute roof is the fp16 peak
+    peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
+    if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS}
     else:
-        roof = {"bound": "mfma", "achieved": tfs, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tfs / FP32_PEAK_TFLOPS}
-    roof["traffic"] = measured_traffic(name)
+        roof = {"bound": "mfma", "achieved": tfs, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": tfs / peak_tf}
+    roof["traffic"] = measured_traffic(name, path)
     med = statistics.median(per_launch_ms)
     extra = {
         "graph_replay": graphed,
@@ -162,7 +170,8 @@ def gpu_leg(name: str, steps: int, warmup: int):
         "per_launch_event_us_p90": float(np.percentile(per_launch_ms, 90)) * 1e3,
         "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9,
         "tflops_at_event_median": wl.flops() / (med * 1e-3) / 1e12,
-        "path": pkg.w4a16_select_path(wl.M, wl.N, wl.K),
+        "path": path if path != "auto" else
+        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)],
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "fp32_frac": tfs / FP32_PEAK_TFLOPS,
     }
@@ -236,7 +245,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_gate_up",
-                    help="one of %s, or 'all'" % ", ".join(workloads.ORDER))
+                    help="comma-separated names from %s, or 'all'" % ", ".join(workloads.ORDER))
+    ap.add_argument("--path", default="auto",
+                    help="kernel path(s), comma-separated: auto, gemv, tile, split")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -248,16 +259,24 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    names = workloads.ORDER if args.workload == "all" else [args.workload]
-    for name in names:
+    names = workloads.ORDER if args.workload == "all" else args.workload.split(",")
+    paths = args.path.split(",")
+    for p in paths:
+        if p not in PATH_NAMES:
+            ap.error(f"unknown path {p!r}")
+    for name, path in [(n, p) for n in names for p in paths]:
         wl = workloads.WORKLOADS[name]
         steps = args.steps if wl.M < 1024 else max(5, min(args.steps, 20))
-        print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps}", file=sys.stderr, flush=True)
-        value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup)
+        print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps} path={path}",
+              file=sys.stderr, flush=True)
+        value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup, path)
+        # arithmetic type: fp32 FMA/MFMA, or fp16 matrix products of two fp16
+        # activation limbs and exact weight codes with fp32 accumulation
+        dtype = "f16x2-limb/f32-acc" if path == "split" else "f32"
         line = {
             "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
             "config": {"workload": name, "M": wl.M, "K": wl.K, "N": wl.N, "group": 32,
                        "note": wl.note, "parallelism": "none (1 GPU)"},
             "roofline": roof,

@@ -64,6 +64,8 @@ extern "C" {
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
 #define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV, x in VGPRs */
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
+#define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
+                                 exact (q - 8) codes and two fp16 limbs of each activation */
 
 /* Version of this ABI (W4A16_ABI_VERSION of the library that was built). */
 int w4a16_abi_version(void);
@@ -94,8 +96,10 @@ int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, floa
                int64_t M, int64_t N, int64_t K, int32_t group, void *stream);
 
 /*
- * As w4a16_gemm, but with the kernel path forced (one of W4A16_PATH_*); every
- * path accepts every valid shape.  For tests and measurement.
+ * As w4a16_gemm, but with the kernel path forced (W4A16_PATH_AUTO, _GEMV or
+ * _TILE; W4A16_PATH_SPLIT needs a workspace and is refused here with
+ * W4A16_ERR_ARG).  Every path accepts every valid shape.  For tests and
+ * measurement.
  */
 int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path,
@@ -103,6 +107,35 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
 
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Workspace bytes w4a16_gemm_split needs for this shape (0 if the shape is
+ * invalid).  It holds the activation limbs (4*M*K bytes), per-row exponents,
+ * split-K partial tiles and counters.
+ */
+size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Y = X . dequant(qweight, scales)^T on the fp16 matrix cores with fp32
+ * accumulation: each weight code (nibble - 8) is exact in fp16; each row of X is
+ * scaled by a power of two (max |x| into [2^14, 2^15)) and split into two fp16
+ * limbs whose sum holds 22 significant bits of every activation (relative error
+ * <= 2^-23); the products are exact in fp32 and accumulated in fp32, one fp32
+ * FMA per group applies the group scale, and the row's power of two is undone
+ * exactly at the store.  A second kernel-side reading of the same operation
+ * the pages define (fp32 activations, int4 weights, fp32 accumulation), for
+ * compute-bound shapes.
+ *
+ * `workspace` is a DEVICE buffer owned by the caller, 256-byte aligned, of at
+ * least w4a16_split_workspace_bytes(M, N, K) bytes, not overlapping any other
+ * argument; its contents need no initialisation and are scratch on return.
+ * Two calls that share a workspace must not run concurrently.  Enqueues two
+ * kernels on `stream`.  Errors as w4a16_gemm, plus W4A16_ERR_ARG for a NULL,
+ * misaligned, too small or overlapping workspace.
+ */
+int w4a16_gemm_split(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                     int64_t M, int64_t N, int64_t K, int32_t group, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

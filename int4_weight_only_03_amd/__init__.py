@@ -5,11 +5,14 @@ from .binding import (  # noqa: F401
     W4A16_PATH_AUTO,
     W4A16_PATH_GEMV,
     W4A16_PATH_TILE,
+    W4A16_PATH_SPLIT,
     W4A16Error,
     load,
     w4a16_abi_version,
     w4a16_gemm,
     w4a16_gemm_path,
+    w4a16_gemm_split,
+    w4a16_split_workspace_bytes,
     w4a16_quantize,
     w4a16_select_path,
     w4a16_status_str,

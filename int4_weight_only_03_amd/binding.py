@@ -23,6 +23,7 @@ W4A16_OK = 0
 W4A16_PATH_AUTO = 0
 W4A16_PATH_GEMV = 1
 W4A16_PATH_TILE = 2
+W4A16_PATH_SPLIT = 3
 
 _lib = None
 
@@ -45,6 +46,11 @@ _SIGS = {
                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                          ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_select_path": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
+    "w4a16_split_workspace_bytes": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64],
+                                    ctypes.c_size_t),
+    "w4a16_gemm_split": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
 }
 
 
@@ -142,6 +148,48 @@ def w4a16_gemm_path(X, qweight, scales, Y=None, path: int = W4A16_PATH_AUTO, str
                                 _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_path")
+    return Y
+
+
+def w4a16_split_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().w4a16_split_workspace_bytes(M, N, K))
+
+
+def _check_operands(X, qweight, scales, Y):
+    import torch
+    X = _dev(X, torch.float32, "X")
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    if X.dim() != 2 or qweight.dim() != 2 or scales.dim() != 2:
+        raise ValueError("X, qweight and scales must be 2-D")
+    M, K = X.shape
+    N = qweight.shape[0]
+    if K % 8 or qweight.shape[1] != K // 8 or tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError(f"shapes disagree: X {tuple(X.shape)}, qweight "
+                         f"{tuple(qweight.shape)}, scales {tuple(scales.shape)}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    return X, qweight, scales, Y, M, N, K
+
+
+def w4a16_gemm_split(X, qweight, scales, Y=None, workspace=None, stream=None):
+    """Split-precision path; `workspace` is a uint8 device tensor of at least
+    w4a16_split_workspace_bytes(M, N, K) bytes (allocated here if None)."""
+    import torch
+    X, qweight, scales, Y, M, N, K = _check_operands(X, qweight, scales, Y)
+    need = w4a16_split_workspace_bytes(M, N, K) if M and N else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    workspace = _dev(workspace, torch.uint8, "workspace")
+    st = load().w4a16_gemm_split(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                                 Y.data_ptr(), M, N, K, GROUP, workspace.data_ptr(),
+                                 workspace.numel(), _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_split")
     return Y
 
 

@@ -21,8 +21,11 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["gemv.hip", "tile.hip"]
+DEVICE_SOURCES = ["gemv.hip", "tile.hip", "split.hip"]
 HOST_SOURCES = ["w4a16_api.cpp"]
+# per-source options: the split path's MFMA results stay in VGPRs (the scale
+# FMAs read them directly, no accumulator-register copies)
+EXTRA = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -68,7 +71,8 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in DEVICE_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([cc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o",
+              obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)

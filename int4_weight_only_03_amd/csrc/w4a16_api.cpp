@@ -87,6 +87,29 @@ int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, floa
   return w4a16_gemm_path(X, qweight, scales, Y, M, N, K, group, W4A16_PATH_AUTO, stream);
 }
 
+size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
+  return w4a16::split_workspace_bytes(int(M), int(N), int(K));
+}
+
+int w4a16_gemm_split(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                     int64_t M, int64_t N, int64_t K, int32_t group, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  int st = validate_gemm(X, qweight, scales, Y, M, N, K, group);
+  if (st != W4A16_OK || M == 0 || N == 0) return st;
+  const size_t need = w4a16::split_workspace_bytes(int(M), int(N), int(K));
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W4A16_ERR_ARG;
+  const size_t bx = size_t(M) * size_t(K) * 4, bq = size_t(N) * size_t(K) / 2,
+               bs = size_t(N) * size_t(K / W4A16_GROUP) * 4, by = size_t(M) * size_t(N) * 4;
+  if (overlaps(workspace, need, X, bx) || overlaps(workspace, need, qweight, bq) ||
+      overlaps(workspace, need, scales, bs) || overlaps(workspace, need, Y, by))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_split(X, qweight, scales, Y, int(M), int(N), int(K), workspace,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_quantize(const float *W, int32_t *qweight, float *scales, int64_t N, int64_t K,
                    int32_t group) {
   if (group != W4A16_GROUP) return W4A16_ERR_ARG;

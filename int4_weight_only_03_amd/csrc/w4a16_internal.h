@@ -19,6 +19,18 @@ hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scal
 hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream);
 
+// Split-precision path: fp16 MFMA on exact weight codes and two fp16 limbs of
+// each activation; needs a caller workspace of split_workspace_bytes(M, N, K).
+size_t split_workspace_bytes(int M, int N, int K);
+hipError_t launch_split(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                        int M, int N, int K, void *workspace, hipStream_t stream);
+// The same with the tile width (64 * J columns, J in {1, 2, 4}) and the K
+// split S fixed by the caller instead of chosen by the library's plan.
+size_t split_workspace_bytes_with(int M, int N, int K, int J, int S);
+hipError_t launch_split_with(const float *X, const int32_t *qweight, const float *scales,
+                             float *Y, int M, int N, int K, int J, int S, void *workspace,
+                             hipStream_t stream);
+
 // Largest M the GEMV path is chosen for by default.
 constexpr int kGemvMaxM = 4;
 

@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 
 from int4_weight_only_03_amd import binding  # noqa: E402
 
-PATHS = {"gemv": binding.W4A16_PATH_GEMV, "tile": binding.W4A16_PATH_TILE}
+PATHS = {"gemv": binding.W4A16_PATH_GEMV, "tile": binding.W4A16_PATH_TILE,
+         "split": binding.W4A16_PATH_SPLIT}
 
 
 def say(*a):
@@ -42,9 +43,15 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def gemm(Xd, Qd, Sd, Y=None, path=binding.W4A16_PATH_AUTO):
+    if path == binding.W4A16_PATH_SPLIT:
+        return binding.w4a16_gemm_split(Xd, Qd, Sd, Y)
+    return binding.w4a16_gemm_path(Xd, Qd, Sd, Y, path=path)
+
+
 def run(X, qw, sc, path, dev):
     Xd, Qd, Sd = to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev)
-    Y = binding.w4a16_gemm_path(Xd, Qd, Sd, path=path)
+    Y = gemm(Xd, Qd, Sd, path=path)
     torch.cuda.synchronize()
     return Y.cpu().numpy()
 
@@ -74,23 +81,25 @@ def test_shapes(dev, path, M, N, K):
     check(run(X, qw, sc, PATHS[path], dev), X, qw, sc, f"{path} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("path", ["auto", "split"])
 @pytest.mark.parametrize("name", ["tiny", "decode_gate_up", "decode_down", "verify_tree"])
-def test_named_workloads_every_output(dev, name):
-    say(f"workload {name}")
+def test_named_workloads_every_output(dev, name, path):
+    say(f"workload {name} path={path}")
     X, W = workloads.make(name)
     qw, sc = oracle.quantize(W)
-    Y = run(X, qw, sc, binding.W4A16_PATH_AUTO, dev)
-    check(Y, X, qw, sc, name)
+    Y = run(X, qw, sc, PATHS.get(path, binding.W4A16_PATH_AUTO), dev)
+    check(Y, X, qw, sc, f"{name} {path}")
     # negative control: the unquantized product lies outside the bound
     plain = X.astype(np.float64) @ W.astype(np.float64).T
     assert not oracle.compare(plain, X, qw, sc)["ok"]
 
 
-def test_prefill_sampled(dev):
-    say("workload prefill (sampled)")
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_prefill_sampled(dev, path):
+    say(f"workload prefill (sampled) path={path}")
     X, W = workloads.make("prefill")
     qw, sc = oracle.quantize(W)
-    Y = run(X, qw, sc, binding.W4A16_PATH_AUTO, dev)
+    Y = run(X, qw, sc, PATHS.get(path, binding.W4A16_PATH_AUTO), dev)
     assert np.all(np.isfinite(Y))
     rng = np.random.default_rng(123)
     M, N = Y.shape
@@ -146,11 +155,49 @@ def test_no_write_outside_y(dev, path):
     pad = 4096
     buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
     Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
-    binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y, PATHS[path])
+    gemm(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y, PATHS[path])
     torch.cuda.synchronize()
     host = buf.cpu().numpy().view(np.uint32)
     assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
     check(Y.cpu().numpy(), X, qw, sc, f"guarded {path}")
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 45, 96), (1, 100, 7168), (70, 300, 2080)])
+def test_split_stays_inside_its_workspace(dev, M, N, K):
+    # the workspace is scratch: nothing past the size the library asks for is
+    # written, and the result does not depend on what the workspace held
+    say(f"split workspace guard M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M + N + K)
+    qw, sc = oracle.quantize(W)
+    need = binding.w4a16_split_workspace_bytes(M, N, K)
+    tail = 65536
+    ws = torch.full((need + tail,), 0xA5, dtype=torch.uint8, device=dev)
+    Xd, Qd, Sd = to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev)
+    a = binding.w4a16_gemm_split(Xd, Qd, Sd, workspace=ws)
+    ws[:need].fill_(0xFF)  # NaN bit patterns everywhere in the used part
+    b = binding.w4a16_gemm_split(Xd, Qd, Sd, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(ws[need:].cpu().numpy() == 0xA5)
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+    check(a.cpu().numpy(), X, qw, sc, f"split guarded {M}x{N}x{K}")
+
+
+def test_split_row_scaling_extremes(dev):
+    # rows spanning the fp32 range: tiny, huge, zero, mixed magnitudes in a row
+    rng = np.random.default_rng(11)
+    M, N, K = 6, 70, 512
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[0] *= np.float32(1e-30)
+    X[1] *= np.float32(1e30)
+    X[2] = 0.0
+    X[3, ::7] *= np.float32(1e6)
+    X[4, 5] = np.float32(3e-39)  # a subnormal among normal values
+    X[5] = np.float32(2.0 ** -140) * rng.integers(1, 9, K)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, binding.W4A16_PATH_SPLIT, dev)
+    check(Y, X, qw, sc, "split row extremes")
+    assert np.all(Y[2] == 0.0)
 
 
 def test_empty_is_noop(dev):

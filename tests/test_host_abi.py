@@ -21,7 +21,8 @@ OK, ARG, SHAPE, ALIGN, NONFINITE, HIP = 0, 1, 2, 3, 4, 5
 def test_exports_every_declared_symbol(lib):
     names = binding.header_functions()
     assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
-            "w4a16_abi_version", "w4a16_select_path"} <= set(names)
+            "w4a16_abi_version", "w4a16_select_path", "w4a16_gemm_split",
+            "w4a16_split_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     assert lib.w4a16_abi_version() == 1
@@ -136,6 +137,43 @@ def test_gemm_empty_is_a_noop(lib):
     assert _call(lib, None, None, None, None, 0, 0, 32, path=2) == OK
     # ...but K is still validated
     assert _call(lib, None, None, None, None, 0, 8, 40) == SHAPE
+
+
+W_ = BASE + (4 << 32)  # fake workspace
+
+
+def _split(lib, X, Q, S, Y, M, N, K, ws=W_, ws_bytes=None, group=32):
+    if ws_bytes is None:
+        ws_bytes = lib.w4a16_split_workspace_bytes(M, N, K)
+    return lib.w4a16_gemm_split(X, Q, S, Y, M, N, K, group, ws, ws_bytes, None)
+
+
+def test_split_workspace_size(lib):
+    ws = lib.w4a16_split_workspace_bytes
+    assert ws(0, 8, 64) == 0 and ws(1, 0, 64) == 0 and ws(1, 8, 48) == 0 and ws(1, 8, 0) == 0
+    for M, N, K in [(1, 1, 32), (5, 300, 2048), (64, 4096, 7168), (4096, 4096, 7168)]:
+        b = ws(M, N, K)
+        # at least the two fp16 limbs of every activation plus one exponent per row
+        assert b >= 4 * M * K + 4 * M and b % 256 == 0
+    assert ws(128, 4096, 7168) >= ws(64, 4096, 7168)
+
+
+def test_split_rejects_bad_workspace(lib):
+    M, N, K = 3, 40, 256
+    need = lib.w4a16_split_workspace_bytes(M, N, K)
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=None) == ARG
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=W_ + 128) == ARG      # not 256-aligned
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws_bytes=need - 1) == ARG
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=X_) == ARG            # overlaps X
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=Y_ - 256) == ARG      # overlaps Y
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=Q_) == ARG            # overlaps qweight
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, ws=S_) == ARG            # overlaps scales
+    # operand errors are those of w4a16_gemm
+    assert _split(lib, X_, Q_, S_, Y_, M, N, 48) == SHAPE
+    assert _split(lib, X_ + 4, Q_, S_, Y_, M, N, K) == ALIGN
+    assert _split(lib, X_, Q_, S_, Y_, M, N, K, group=64) == ARG
+    # empty: no workspace needed, nothing launched
+    assert _split(lib, None, None, None, None, 0, N, K, ws=None, ws_bytes=0) == OK
 
 
 def test_binding_refuses_host_tensors(lib):
