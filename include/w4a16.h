@@ -137,6 +137,44 @@ int w4a16_gemm_split(const float *X, const int32_t *qweight, const float *scales
                      int64_t M, int64_t N, int64_t K, int32_t group, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * Bytes of the packed weights w4a16_split_pack writes for an N x K matrix
+ * (0 if the shape is invalid): ceil(N/64) * ceil(K/64) * 2560 bytes, the same
+ * as qweight plus scales up to the padding of N to 64 rows and of the group
+ * count to even.
+ */
+size_t w4a16_split_pack_bytes(int64_t N, int64_t K);
+
+/*
+ * One-time repack of qweight[N][K/8] and scales[N][K/32] (DEVICE memory, the
+ * layouts above) into the split path's kernel-private layout, `packed` (DEVICE
+ * memory owned by the caller, 16-byte aligned, at least
+ * w4a16_split_pack_bytes(N, K) bytes, overlapping no input).  The optional
+ * repack into a kernel-private layout that the pages allow for the weights;
+ * it moves bits only (the weights and scales are copied unchanged).  Layout,
+ * for slab s of 64 rows and stage t of 2 groups (S = ceil(N/64) slabs,
+ * T = ceil(K/64) stages):
+ *   bytes [0, S*T*2048): at ((s*T + t)*2 + g)*64 + r chunks of 16 bytes, the
+ *     4 words of group 2t+g of row 64s+r;
+ *   then S*T*512 bytes: at float index (s*T + t)*128 + 2r + g, its scale.
+ * Rows past N and the group past K/32 (K/32 odd) hold words 0x88888888 (code
+ * 0) and scale 0.  Enqueued on `stream`; errors as w4a16_gemm (W4A16_ERR_ARG
+ * for a NULL, misaligned, too small or overlapping `packed`).
+ */
+int w4a16_split_pack(const int32_t *qweight, const float *scales, int64_t N, int64_t K,
+                     int32_t group, void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * w4a16_gemm_split on weights packed by w4a16_split_pack(..., N, K, ...):
+ * the same result, bit for bit, as w4a16_gemm_split on the unpacked weights,
+ * with every weight and scale copy reading whole cache lines.  Workspace as
+ * for w4a16_gemm_split (w4a16_split_workspace_bytes(M, N, K)).  X must not
+ * overlap Y; `packed` is 16-byte aligned.
+ */
+int w4a16_gemm_split_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                            int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,14 @@ _SIGS = {
     "w4a16_gemm_split": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_split_pack_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
+    "w4a16_split_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
+                         ctypes.c_int),
+    "w4a16_gemm_split_packed": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
+                                ctypes.c_int),
 }
 
 
@@ -190,6 +198,61 @@ def w4a16_gemm_split(X, qweight, scales, Y=None, workspace=None, stream=None):
                                  workspace.numel(), _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_split")
+    return Y
+
+
+def w4a16_split_pack_bytes(N: int, K: int) -> int:
+    return int(load().w4a16_split_pack_bytes(N, K))
+
+
+def w4a16_split_pack(qweight, scales, packed=None, stream=None):
+    """Repack device qweight/scales for w4a16_gemm_split_packed (uint8 tensor)."""
+    import torch
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    N, K8 = qweight.shape
+    K = 8 * K8
+    if tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError(f"shapes disagree: qweight {tuple(qweight.shape)}, "
+                         f"scales {tuple(scales.shape)}")
+    need = w4a16_split_pack_bytes(N, K) if N else 0
+    if packed is None:
+        packed = torch.empty(max(need, 1), dtype=torch.uint8, device=qweight.device)
+    packed = _dev(packed, torch.uint8, "packed")
+    st = load().w4a16_split_pack(qweight.data_ptr(), scales.data_ptr(), N, K, GROUP,
+                                 packed.data_ptr(), packed.numel(),
+                                 _stream_ptr(stream, qweight.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_split_pack")
+    return packed
+
+
+def w4a16_gemm_split_packed(X, packed, N: int, Y=None, workspace=None, stream=None):
+    """Split path on weights from w4a16_split_pack (N rows); workspace as for
+    w4a16_gemm_split (allocated here if None)."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    packed = _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    M, K = X.shape
+    if packed.numel() < w4a16_split_pack_bytes(N, K):
+        raise ValueError("packed buffer smaller than w4a16_split_pack_bytes(N, K)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    need = w4a16_split_workspace_bytes(M, N, K) if M and N else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    workspace = _dev(workspace, torch.uint8, "workspace")
+    st = load().w4a16_gemm_split_packed(X.data_ptr(), packed.data_ptr(), Y.data_ptr(), M, N, K,
+                                        GROUP, workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_split_packed")
     return Y
 
 

@@ -110,6 +110,54 @@ int w4a16_gemm_split(const float *X, const int32_t *qweight, const float *scales
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+size_t w4a16_split_pack_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
+  return w4a16::split_pack_bytes(int(N), int(K));
+}
+
+int w4a16_split_pack(const int32_t *qweight, const float *scales, int64_t N, int64_t K,
+                     int32_t group, void *packed, size_t packed_bytes, void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (N == 0) return W4A16_OK;
+  if (!qweight || !scales || !packed) return W4A16_ERR_ARG;
+  if (!aligned(qweight, 16) || !aligned(scales, 4)) return W4A16_ERR_ALIGN;
+  const size_t need = w4a16::split_pack_bytes(int(N), int(K));
+  if (!aligned(packed, 16) || packed_bytes < need) return W4A16_ERR_ARG;
+  const size_t bq = size_t(N) * size_t(K) / 2, bs = size_t(N) * size_t(K / W4A16_GROUP) * 4;
+  if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_split_pack(qweight, scales, packed, int(N), int(K),
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm_split_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                            int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!X || !packed || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4)) return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(M) * size_t(K) * 4, by = size_t(M) * size_t(N) * 4;
+  const size_t bp = w4a16::split_pack_bytes(int(N), int(K));
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
+  const size_t need = w4a16::split_workspace_bytes(int(M), int(N), int(K));
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W4A16_ERR_ARG;
+  if (overlaps(workspace, need, X, bx) || overlaps(workspace, need, packed, bp) ||
+      overlaps(workspace, need, Y, by))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_split_packed(X, packed, Y, int(M), int(N), int(K), workspace,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_quantize(const float *W, int32_t *qweight, float *scales, int64_t N, int64_t K,
                    int32_t group) {
   if (group != W4A16_GROUP) return W4A16_ERR_ARG;

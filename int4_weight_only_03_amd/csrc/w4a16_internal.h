@@ -24,12 +24,20 @@ hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scal
 size_t split_workspace_bytes(int M, int N, int K);
 hipError_t launch_split(const float *X, const int32_t *qweight, const float *scales, float *Y,
                         int M, int N, int K, void *workspace, hipStream_t stream);
-// The same with the tile width (64 * J columns, J in {1, 2, 4}) and the K
-// split S fixed by the caller instead of chosen by the library's plan.
-size_t split_workspace_bytes_with(int M, int N, int K, int J, int S);
-hipError_t launch_split_with(const float *X, const int32_t *qweight, const float *scales,
-                             float *Y, int M, int N, int K, int J, int S, void *workspace,
-                             hipStream_t stream);
+// Packed weights for the split path (one-time repack of qweight and scales
+// into the kernel's stage layout) and the GEMM on them.
+size_t split_pack_bytes(int N, int K);
+hipError_t launch_split_pack(const int32_t *qweight, const float *scales, void *packed, int N,
+                             int K, hipStream_t stream);
+hipError_t launch_split_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
+                               void *workspace, hipStream_t stream);
+// The split path with the tile (64 x 16 J WN), the K split S and the pipeline
+// depth D fixed by the caller instead of chosen by the library's plan;
+// `weights` is qweight (scales separate) or, with `packed`, a packed buffer.
+size_t split_workspace_bytes_with(int M, int N, int K, int J, int WN, int S);
+hipError_t launch_split_with(const float *X, const void *weights, const float *scales, bool packed,
+                             float *Y, int M, int N, int K, int J, int WN, int S, int D,
+                             void *workspace, hipStream_t stream);
 
 // Largest M the GEMV path is chosen for by default.
 constexpr int kGemvMaxM = 4;

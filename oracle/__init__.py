@@ -21,4 +21,8 @@ from .w4a16_ref import (  # noqa: F401
     bound,
     compare,
     compare_entries,
+    pack_split,
+    unpack_split,
+    SLAB,
+    STAGE_GROUPS,
 )

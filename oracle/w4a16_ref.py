@@ -38,6 +38,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
   or so tiny that max|w|/7 underflows) gets q = 0 everywhere.
 * Non-finite weights are rejected; K % 32 != 0 is rejected (no padding).
 * Dequantized weight = fl32((nibble - 8) * scale), one rounded fp32 multiply.
+* Repack: the pages allow an optional one-time repack of the weights into a
+  kernel-private layout.  ``pack_split`` writes the library's split-path
+  layout from its index formula (64-row slabs, stages of 2 groups, zero code
+  and zero scale as padding); it only moves bits, so the library's repack
+  must match it byte for byte.
 * Product: accumulated in fp64 (every fp32 x fp32 product is exact in fp64).
   An fp32 result is accepted iff |Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6
   elementwise, with w the dequantized fp32 weight and the sum in fp64.
@@ -139,6 +144,60 @@ def dequantize(qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # the product, accumulated in fp64 ("dequantize-then-multiply")
 # --------------------------------------------------------------------------
+
+SLAB = 64          # rows per slab of the split-path packed layout
+STAGE_GROUPS = 2   # groups per stage
+
+
+def pack_split(qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed split-path layout of (qweight[N][K/8], scales[N][K/32]) as bytes.
+
+    For slab s (rows 64s..64s+63) and stage t (groups 2t, 2t+1), with S slabs
+    and T stages: 16-byte chunk ((s*T + t)*2 + g)*64 + r holds the 4 words of
+    group 2t+g of row 64s+r; after all S*T*2048 such bytes, float
+    (s*T + t)*128 + 2r + g holds that group's scale.  Rows past N and the group
+    past G = K/32 (odd G) hold words 0x88888888 (every nibble 8, code 0) and
+    scale 0.0.
+    """
+    qweight = np.ascontiguousarray(qweight).view(np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=_F32)
+    N, G = scales.shape
+    if qweight.shape != (N, 4 * G):
+        raise ValueError("qweight and scales disagree")
+    S = -(-N // SLAB)
+    T = -(-G // STAGE_GROUPS)
+    words = np.full((S, T, STAGE_GROUPS, SLAB, 4), 0x88888888, dtype=np.uint32)
+    sc = np.zeros((S, T, SLAB, STAGE_GROUPS), dtype=_F32)
+    for n in range(N):                      # plain loops: row n, group gg
+        s_, r = divmod(n, SLAB)
+        for gg in range(G):
+            t, g = divmod(gg, STAGE_GROUPS)
+            words[s_, t, g, r, :] = qweight[n, 4 * gg:4 * gg + 4]
+            sc[s_, t, r, g] = scales[n, gg]
+    return np.concatenate([words.reshape(-1).view(np.uint8), sc.reshape(-1).view(np.uint8)])
+
+
+def unpack_split(packed: np.ndarray, N: int, K: int) -> tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack_split: (qweight int32 [N][K/8], scales fp32 [N][K/32])."""
+    check_k(K)
+    G = K // GROUP
+    S = -(-N // SLAB)
+    T = -(-G // STAGE_GROUPS)
+    nw = S * T * STAGE_GROUPS * SLAB * 4
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    words = packed[:4 * nw].view(np.uint32).reshape(S, T, STAGE_GROUPS, SLAB, 4)
+    sc = packed[4 * nw:4 * nw + 4 * S * T * SLAB * STAGE_GROUPS].view(_F32).reshape(
+        S, T, SLAB, STAGE_GROUPS)
+    qweight = np.zeros((N, 4 * G), dtype=np.uint32)
+    scales = np.zeros((N, G), dtype=_F32)
+    for n in range(N):
+        s_, r = divmod(n, SLAB)
+        for gg in range(G):
+            t, g = divmod(gg, STAGE_GROUPS)
+            qweight[n, 4 * gg:4 * gg + 4] = words[s_, t, g, r, :]
+            scales[n, gg] = sc[s_, t, r, g]
+    return qweight.view(np.int32), scales
+
 
 def _operands(X, qweight, scales):
     X = np.asarray(X)

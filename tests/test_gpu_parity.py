@@ -22,8 +22,9 @@ pytestmark = pytest.mark.gpu
 
 from int4_weight_only_03_amd import binding  # noqa: E402
 
+PACKED = -1  # the split path on weights repacked by w4a16_split_pack
 PATHS = {"gemv": binding.W4A16_PATH_GEMV, "tile": binding.W4A16_PATH_TILE,
-         "split": binding.W4A16_PATH_SPLIT}
+         "split": binding.W4A16_PATH_SPLIT, "packed": PACKED}
 
 
 def say(*a):
@@ -46,6 +47,9 @@ def to_dev(a, dev):
 def gemm(Xd, Qd, Sd, Y=None, path=binding.W4A16_PATH_AUTO):
     if path == binding.W4A16_PATH_SPLIT:
         return binding.w4a16_gemm_split(Xd, Qd, Sd, Y)
+    if path == PACKED:
+        packed = binding.w4a16_split_pack(Qd, Sd)
+        return binding.w4a16_gemm_split_packed(Xd, packed, Qd.shape[0], Y)
     return binding.w4a16_gemm_path(Xd, Qd, Sd, Y, path=path)
 
 
@@ -81,7 +85,7 @@ def test_shapes(dev, path, M, N, K):
     check(run(X, qw, sc, PATHS[path], dev), X, qw, sc, f"{path} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("path", ["auto", "split"])
+@pytest.mark.parametrize("path", ["auto", "split", "packed"])
 @pytest.mark.parametrize("name", ["tiny", "decode_gate_up", "decode_down", "verify_tree"])
 def test_named_workloads_every_output(dev, name, path):
     say(f"workload {name} path={path}")
@@ -94,7 +98,7 @@ def test_named_workloads_every_output(dev, name, path):
     assert not oracle.compare(plain, X, qw, sc)["ok"]
 
 
-@pytest.mark.parametrize("path", ["auto", "split"])
+@pytest.mark.parametrize("path", ["auto", "split", "packed"])
 def test_prefill_sampled(dev, path):
     say(f"workload prefill (sampled) path={path}")
     X, W = workloads.make("prefill")
@@ -198,6 +202,30 @@ def test_split_row_scaling_extremes(dev):
     Y = run(X, qw, sc, binding.W4A16_PATH_SPLIT, dev)
     check(Y, X, qw, sc, "split row extremes")
     assert np.all(Y[2] == 0.0)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (70, 96), (130, 224), (64, 7168), (257, 160)])
+def test_split_pack_matches_oracle_bytes(dev, N, K):
+    say(f"split pack N={N} K={K}")
+    _, W = workloads.random_case(1, N, K, seed=N + 7 * K)
+    qw, sc = oracle.quantize(W)
+    packed = binding.w4a16_split_pack(to_dev(qw, dev), to_dev(sc, dev))
+    torch.cuda.synchronize()
+    want = oracle.pack_split(qw, sc)
+    got = packed.cpu().numpy()
+    assert got.size == want.size and np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 70, 96), (64, 300, 2080), (130, 600, 224), (1, 100, 7168)])
+def test_packed_equals_split_bitwise(dev, M, N, K):
+    # the same plan and the same arithmetic on repacked operands: identical bits
+    say(f"packed vs split M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M + N + K + 1)
+    qw, sc = oracle.quantize(W)
+    a = run(X, qw, sc, binding.W4A16_PATH_SPLIT, dev)
+    b = run(X, qw, sc, PACKED, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    check(b, X, qw, sc, f"packed {M}x{N}x{K}")
 
 
 def test_empty_is_noop(dev):

@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(lib):
     names = binding.header_functions()
     assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
             "w4a16_abi_version", "w4a16_select_path", "w4a16_gemm_split",
-            "w4a16_split_workspace_bytes"} <= set(names)
+            "w4a16_split_workspace_bytes", "w4a16_split_pack", "w4a16_split_pack_bytes",
+            "w4a16_gemm_split_packed"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     assert lib.w4a16_abi_version() == 1
@@ -174,6 +175,42 @@ def test_split_rejects_bad_workspace(lib):
     assert _split(lib, X_, Q_, S_, Y_, M, N, K, group=64) == ARG
     # empty: no workspace needed, nothing launched
     assert _split(lib, None, None, None, None, 0, N, K, ws=None, ws_bytes=0) == OK
+
+
+def test_split_pack_size_and_errors(lib):
+    pb = lib.w4a16_split_pack_bytes
+    assert pb(0, 64) == 0 and pb(8, 48) == 0 and pb(8, 0) == 0
+    assert pb(1, 32) == 2560 and pb(64, 64) == 2560 and pb(65, 96) == 2 * 2 * 2560
+    assert pb(4096, 7168) == 64 * 112 * 2560
+    P_ = BASE + (5 << 32)
+    need = pb(70, 224)
+    pack = lambda q, s, n, k, p, nb, group=32: lib.w4a16_split_pack(q, s, n, k, group, p, nb, None)
+    assert pack(Q_, S_, 70, 224, P_, need - 1) == ARG
+    assert pack(Q_, S_, 70, 224, None, need) == ARG
+    assert pack(Q_, S_, 70, 224, P_ + 8, need) == ARG   # packed not 16-byte aligned
+    assert pack(Q_ + 4, S_, 70, 224, P_, need) == ALIGN
+    assert pack(Q_, S_, 70, 224, Q_, need) == ARG       # overlaps qweight
+    assert pack(Q_, S_, 70, 48, P_, need) == SHAPE
+    assert pack(Q_, S_, 70, 224, P_, need, group=64) == ARG
+    assert pack(None, None, 0, 224, None, 0) == OK      # N == 0: nothing to do
+
+
+def test_split_packed_gemm_errors(lib):
+    P_ = BASE + (5 << 32)
+    M, N, K = 3, 40, 256
+    need = lib.w4a16_split_workspace_bytes(M, N, K)
+    g = lambda x, p, y, ws=W_, nb=need, m=M, k=K, group=32: lib.w4a16_gemm_split_packed(
+        x, p, y, m, N, k, group, ws, nb, None)
+    assert g(X_, P_, Y_, ws=None) == ARG
+    assert g(X_, P_, Y_, nb=need - 1) == ARG
+    assert g(X_, P_, Y_, ws=W_ + 64) == ARG
+    assert g(X_, P_ + 4, Y_) == ALIGN
+    assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(X_, P_, X_ + 64) == ARG                    # Y overlaps X
+    assert g(X_, P_, P_) == ARG                         # Y overlaps packed
+    assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_, Y_, group=16) == ARG
+    assert g(None, None, None, ws=None, nb=0, m=0) == OK
 
 
 def test_binding_refuses_host_tensors(lib):
