@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A16 group-quantized GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME[,NAME]|all]
+                    [--path auto|gemv|tile|split|packed[,...]] [--no-cpu]
 
-A step is one call of w4a16_gemm (the whole hot path: validate, launch,
-unpack + dequant + fp32 contraction + reduction + store) on one batch of
-synthetic input.  Inputs are resident in HBM before the timed region starts.
+A step is one call of the chosen entry point (the whole hot path: validate,
+launch, unpack + dequant + contraction + reduction + store) on one batch of
+synthetic input: w4a16_gemm / w4a16_gemm_path for auto, gemv and tile;
+w4a16_gemm_split (activation prep, fp16-MFMA contraction, split-K reduce) for
+split; w4a16_gemm_split_packed for packed, whose one-time weight repack runs
+before the timed region and is reported on its own (repack_ms_one_time).  Inputs are resident in HBM before the timed region starts.
 Copies of {X, qweight, scales, Y} rotate so that every step reads cold HBM
 (the copies together are at least twice the 256 MB Infinity Cache).  The K
 timed steps are captured once in a HIP graph and replayed, so the host's
@@ -39,31 +43,33 @@ FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["int4_weight_only_03_amd/csrc/gemv.hip", "int4_weight_only_03_amd/csrc/tile.hip",
-                  "int4_weight_only_03_amd/csrc/split.hip",
-                  "int4_weight_only_03_amd/csrc/w4a16_api.cpp"]
-PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3}
+CSRC = "int4_weight_only_03_amd/csrc/"
+PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4}
+SPLIT_PATHS = ("split", "packed")
+# the sources whose kernels a path runs (the C-ABI layer dispatches every path)
+PATH_SOURCES = {"gemv": ["gemv.hip"], "tile": ["tile.hip"], "split": ["split.hip"],
+                "packed": ["split.hip"]}
 
 
-def kernel_source_hash() -> str:
+def source_hash(path: str) -> str:
+    """Hash of the sources behind a (resolved) path; counter data older than it is void."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in PATH_SOURCES[path] + ["w4a16_api.cpp"]:
+        with open(os.path.join(ROOT, CSRC, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, path: str):
-    """HBM bytes per call from the committed counter runs, if the kernels are unchanged."""
+    """HBM bytes per call from the committed counter runs, if those kernels are unchanged."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    entry = rec.get("entries", {}).get(f"{workload}/{path}")
+    if entry is None or entry.get("source_hash") != source_hash(path):
         return None
-    key = workload if path == "auto" else f"{workload}/{path}"
-    entry = rec.get("workloads", {}).get(key)
-    return None if entry is None else entry.get("bytes_per_launch")
+    return entry.get("bytes_per_launch")
 
 
 def metric_in_gbs(wl) -> bool:
@@ -91,14 +97,29 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     del Xd, Qd, Sd
     stream = torch.cuda.current_stream(dev)
     code = PATH_NAMES[path]
-    if code == pkg.W4A16_PATH_SPLIT:
+    repack_ms = None
+    if path in SPLIT_PATHS:
         # one caller-owned workspace, reused by every (stream-ordered) step
         ws = torch.empty(pkg.w4a16_split_workspace_bytes(wl.M, wl.N, wl.K), dtype=torch.uint8,
                          device=dev)
-
+    if path == "split":
         def step(i):
             x, q, s, y = sets[i % copies]
             pkg.w4a16_gemm_split(x, q, s, y, workspace=ws)
+    elif path == "packed":
+        # the one-time repack (outside the timed region, timed on its own)
+        packs = [pkg.w4a16_split_pack(q, s) for (_, q, s, _) in sets]
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        pkg.w4a16_split_pack(sets[0][1], sets[0][2], packs[0])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        repack_ms = ev0.elapsed_time(ev1)
+
+        def step(i):
+            x, _, _, y = sets[i % copies]
+            pkg.w4a16_gemm_split_packed(x, packs[i % copies], wl.N, y, workspace=ws)
     else:
         def step(i):
             x, q, s, y = sets[i % copies]
@@ -149,7 +170,7 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
     value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
-    split = code == pkg.W4A16_PATH_SPLIT
+    split = path in SPLIT_PATHS
     # the split path issues fp16 matrix instructions: its compute roof is the fp16 peak
     peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
     if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
@@ -158,7 +179,9 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     else:
         roof = {"bound": "mfma", "achieved": tfs, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": tfs / peak_tf}
-    roof["traffic"] = measured_traffic(name, path)
+    resolved = path if path != "auto" else \
+        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)]
+    roof["traffic"] = measured_traffic(name, resolved)
     med = statistics.median(per_launch_ms)
     extra = {
         "graph_replay": graphed,
@@ -170,9 +193,9 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         "per_launch_event_us_p90": float(np.percentile(per_launch_ms, 90)) * 1e3,
         "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9,
         "tflops_at_event_median": wl.flops() / (med * 1e-3) / 1e12,
-        "path": path if path != "auto" else
-        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)],
+        "path": resolved,
         "hbm_frac": gbs / HBM_PEAK_GBS,
+        "repack_ms_one_time": repack_ms,
         "fp32_frac": tfs / FP32_PEAK_TFLOPS,
     }
     y0 = sets[0][3].cpu().numpy()
@@ -272,7 +295,7 @@ def main():
         value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup, path)
         # arithmetic type: fp32 FMA/MFMA, or fp16 matrix products of two fp16
         # activation limbs and exact weight codes with fp32 accumulation
-        dtype = "f16x2-limb/f32-acc" if path == "split" else "f32"
+        dtype = "f16x2-limb/f32-acc" if path in SPLIT_PATHS else "f32"
         line = {
             "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

@@ -600,7 +600,7 @@ SplitPlan make_plan(int M, int N, int G, int J, int WN, int S, int D) {
 SplitPlan plan_split(int M, int N, int G) {
   const int stages = (G + 1) / 2;
   const int m_tiles = (M + kBM - 1) / kBM;
-  if (long(m_tiles) * ((N + 511) / 512) >= 256) return make_plan(M, N, G, 4, 8, 1, 3);
+  if (long(m_tiles) * ((N + 511) / 512) >= 256) return make_plan(M, N, G, 4, 8, 1, 4);
   SplitPlan best{};
   double best_cost = 0.0;
   for (int J : {4, 2, 1}) {
@@ -610,7 +610,9 @@ SplitPlan plan_split(int M, int N, int G) {
     const double kq = double(stages) * kStageK / S;  // k per workgroup
     const double bn = 64.0 * J;
     const double mfma_us = kBM * bn * kq * 4.0 / 4.9e6;  // two limbs, ~half of peak
-    const double l2_us = (kBM * kq * 4.0 + bn * kq * 0.625) / 1.5e5;
+    // ~50 GB/s of L2-to-CU traffic per workgroup: what the K-split sweeps at
+    // M = 64 measure once a workgroup's activation slice exceeds ~200 KB
+    const double l2_us = (kBM * kq * 4.0 + bn * kq * 0.625) / 5e4;
     const double rounds = std::ceil(double(m_tiles) * n_tiles * S / 256.0);
     double cost = rounds * std::max(mfma_us, l2_us);
     if (S > 1) cost += 2.0 * S * double(M) * N * 4.0 / 5e6 + 1.2;
