@@ -9,7 +9,9 @@ launch, unpack + dequant + contraction + reduction + store) on one batch of
 synthetic input: w4a16_gemm / w4a16_gemm_path for auto, gemv and tile;
 w4a16_gemm_split (activation prep, fp16-MFMA contraction, split-K reduce) for
 split; w4a16_gemm_split_packed for packed, whose one-time weight repack runs
-before the timed region and is reported on its own (repack_ms_one_time).  Inputs are resident in HBM before the timed region starts.
+before the timed region and is reported on its own (repack_ms_one_time);
+w4a16_gemm_swiglu for swiglu (the workload's W read as gate rows then up rows,
+Y = silu(gate) * up, [M][N/2]).  Inputs are resident in HBM before the timed region starts.
 Copies of {X, qweight, scales, Y} rotate so that every step reads cold HBM
 (the copies together are at least twice the 256 MB Infinity Cache).  The K
 timed steps are captured once in a HIP graph and replayed, so the host's
@@ -44,11 +46,11 @@ FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "int4_weight_only_03_amd/csrc/"
-PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4}
+PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5}
 SPLIT_PATHS = ("split", "packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip"], "tile": ["tile.hip"], "split": ["split.hip"],
-                "packed": ["split.hip"]}
+                "packed": ["split.hip"], "swiglu": ["gemv.hip"]}
 
 
 def source_hash(path: str) -> str:
@@ -86,6 +88,8 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     X, W = workloads.make(name)
     qw, sc = pkg.w4a16_quantize(W)            # the library's own host quantizer
     B = wl.algorithmic_bytes()
+    if path == "swiglu":  # Y is [M][N/2]: the gate/up outputs never reach memory
+        B -= 4 * wl.M * (wl.N // 2)
     copies = 1 if B * 2 > 4 * MALL_BYTES else max(1, -(-2 * MALL_BYTES // B))
     if name == "tiny":
         copies = 1                             # cache-resident by nature
@@ -120,6 +124,13 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         def step(i):
             x, _, _, y = sets[i % copies]
             pkg.w4a16_gemm_split_packed(x, packs[i % copies], wl.N, y, workspace=ws)
+    elif path == "swiglu":
+        ys = [torch.empty((wl.M, wl.N // 2), dtype=torch.float32, device=dev)
+              for _ in range(copies)]
+
+        def step(i):
+            x, q, s, _ = sets[i % copies]
+            pkg.w4a16_gemm_swiglu(x, q, s, ys[i % copies])
     else:
         def step(i):
             x, q, s, y = sets[i % copies]
@@ -198,11 +209,11 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         "repack_ms_one_time": repack_ms,
         "fp32_frac": tfs / FP32_PEAK_TFLOPS,
     }
-    y0 = sets[0][3].cpu().numpy()
+    y0 = (ys[0] if path == "swiglu" else sets[0][3]).cpu().numpy()
     return value, unit, ms_per_step, roof, extra, (X, W, y0)
 
 
-def cpu_leg(name: str, gpu_out, budget_s: float = 12.0):
+def cpu_leg(name: str, gpu_out, budget_s: float = 12.0, path: str = "auto"):
     """The oracle, as it stands, timed on the host cores over a bounded sample."""
     import oracle
     try:
@@ -225,7 +236,10 @@ def cpu_leg(name: str, gpu_out, budget_s: float = 12.0):
         Yref = None
         while time.perf_counter() < t_end or not times:
             t0 = time.perf_counter()
-            Yref = oracle.gemm(Xs, qw, sc)            # dequant + fp64 product
+            if path == "swiglu":
+                Yref = oracle.swiglu(Xs, qw, sc)      # dequant + fp64 product + epilogue
+            else:
+                Yref = oracle.gemm(Xs, qw, sc)        # dequant + fp64 product
             times.append(time.perf_counter() - t0)
             if len(times) >= 50:
                 break
@@ -240,8 +254,12 @@ def cpu_leg(name: str, gpu_out, budget_s: float = 12.0):
         value, unit = sample_bytes / t / 1e9, "GB/s"
     else:
         value, unit = sample_flops / t / 1e12, "TFLOP/s"
-    T = oracle.abs_gemm(Xs, qw, sc)
-    err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.bound(T)
+    if path == "swiglu":
+        sample_bytes -= 4 * rows * (wl.N // 2)
+        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.swiglu_bound(Xs, qw, sc)
+    else:
+        T = oracle.abs_gemm(Xs, qw, sc)
+        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.bound(T)
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of X against all {wl.N} weight rows "
                       f"(dequant + fp64 product), median of {len(times)} runs, "
@@ -306,7 +324,7 @@ def main():
         }
         line.update(extra)
         if not args.no_cpu:
-            line["cpu_baseline"] = cpu_leg(name, out)
+            line["cpu_baseline"] = cpu_leg(name, out, path=path)
         print(json.dumps(line), flush=True)
 
 

@@ -105,6 +105,22 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path,
                     void *stream);
 
+/*
+ * Fused gate/up projection with a SwiGLU epilogue, for the decode MLP whose
+ * gate and up projections share one W4A16 matrix ("gate+up (2x2048)" in the
+ * pages' decode configuration; SwiGLU is the engine's MLP activation):
+ * qweight[2F][K/8] and scales[2F][K/32] hold the gate rows 0..F-1 followed by
+ * the up rows F..2F-1, and
+ *     Y[m][j] = silu(g) * u,  g = X[m] . gate_j,  u = X[m] . up_j,
+ *     silu(g) = g / (1 + exp(-g)),
+ * with g and u the same fp32 group-scaled sums as w4a16_gemm and the epilogue
+ * in fp32.  Y is [M][F] (not 2F); the gate/up outputs never reach memory.
+ * Runs on the GEMV kernels (fast for M <= 2; any M accepted).  Errors as
+ * w4a16_gemm with N = 2F.
+ */
+int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                      int64_t M, int64_t F, int64_t K, int32_t group, void *stream);
+
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 

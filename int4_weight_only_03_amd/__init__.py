@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     w4a16_gemm,
     w4a16_gemm_path,
     w4a16_gemm_split,
+    w4a16_gemm_swiglu,
     w4a16_gemm_split_packed,
     w4a16_split_pack,
     w4a16_split_pack_bytes,

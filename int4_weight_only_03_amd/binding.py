@@ -51,6 +51,9 @@ _SIGS = {
     "w4a16_gemm_split": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_gemm_swiglu": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                           ctypes.c_void_p], ctypes.c_int),
     "w4a16_split_pack_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
     "w4a16_split_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
@@ -163,7 +166,7 @@ def w4a16_split_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(load().w4a16_split_workspace_bytes(M, N, K))
 
 
-def _check_operands(X, qweight, scales, Y):
+def _check_operands(X, qweight, scales, Y, allocate=True):
     import torch
     X = _dev(X, torch.float32, "X")
     qweight = _dev(qweight, torch.int32, "qweight")
@@ -176,7 +179,8 @@ def _check_operands(X, qweight, scales, Y):
         raise ValueError(f"shapes disagree: X {tuple(X.shape)}, qweight "
                          f"{tuple(qweight.shape)}, scales {tuple(scales.shape)}")
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+        if allocate:
+            Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     else:
         Y = _dev(Y, torch.float32, "Y")
         if tuple(Y.shape) != (M, N):
@@ -198,6 +202,26 @@ def w4a16_gemm_split(X, qweight, scales, Y=None, workspace=None, stream=None):
                                  workspace.numel(), _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_split")
+    return Y
+
+
+def w4a16_gemm_swiglu(X, qweight, scales, Y=None, stream=None):
+    """Y[M][F] = silu(X . gate^T) * (X . up^T); qweight/scales hold 2F rows (gate, then up)."""
+    import torch
+    X, qweight, scales, _, M, N2, K = _check_operands(X, qweight, scales, None, allocate=False)
+    if N2 % 2:
+        raise ValueError("the gate/up matrix needs an even number of rows")
+    F = N2 // 2
+    if Y is None:
+        Y = torch.empty((M, F), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, F):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, F)}")
+    st = load().w4a16_gemm_swiglu(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                                  Y.data_ptr(), M, F, K, GROUP, _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_swiglu")
     return Y
 
 

@@ -25,8 +25,10 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// N: rows of W; NY: columns of Y (N, or N / 2 for the fused SwiGLU)
 int validate_gemm(const float *X, const int32_t *qweight, const float *scales, float *Y,
-                  int64_t M, int64_t N, int64_t K, int32_t group) {
+                  int64_t M, int64_t N, int64_t K, int32_t group, int64_t NY = -1) {
+  if (NY < 0) NY = N;
   if (group != W4A16_GROUP) return W4A16_ERR_ARG;
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
   if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
@@ -36,7 +38,7 @@ int validate_gemm(const float *X, const int32_t *qweight, const float *scales, f
   if (!aligned(X, 16) || !aligned(qweight, 16) || !aligned(scales, 4) || !aligned(Y, 4))
     return W4A16_ERR_ALIGN;
   const size_t bx = size_t(M) * size_t(K) * 4, bq = size_t(N) * size_t(K) / 2,
-               bs = size_t(N) * size_t(K / W4A16_GROUP) * 4, by = size_t(M) * size_t(N) * 4;
+               bs = size_t(N) * size_t(K / W4A16_GROUP) * 4, by = size_t(M) * size_t(NY) * 4;
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, qweight, bq) || overlaps(Y, by, scales, bs))
     return W4A16_ERR_ARG;
   return W4A16_OK;
@@ -85,6 +87,16 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
 int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, float *Y, int64_t M,
                int64_t N, int64_t K, int32_t group, void *stream) {
   return w4a16_gemm_path(X, qweight, scales, Y, M, N, K, group, W4A16_PATH_AUTO, stream);
+}
+
+int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                      int64_t M, int64_t F, int64_t K, int32_t group, void *stream) {
+  if (F < 0 || F > W4A16_MAX_N / 2) return F < 0 ? W4A16_ERR_ARG : W4A16_ERR_SHAPE;
+  int st = validate_gemm(X, qweight, scales, Y, M, 2 * F, K, group, F);
+  if (st != W4A16_OK || M == 0 || F == 0) return st;
+  hipError_t e = w4a16::launch_gemv_swiglu(X, qweight, scales, Y, int(M), int(F), int(K),
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
 size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -39,6 +39,11 @@ hipError_t launch_split_with(const float *X, const void *weights, const float *s
                              float *Y, int M, int N, int K, int J, int WN, int S, int D,
                              void *workspace, hipStream_t stream);
 
+// Fused gate/up SwiGLU on the GEMV path: W has 2F rows (gate, then up);
+// Y[M][F] = silu(X . gate^T) * (X . up^T).
+hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const float *scales,
+                              float *Y, int M, int F, int K, hipStream_t stream);
+
 // Largest M the GEMV path is chosen for by default.
 constexpr int kGemvMaxM = 4;
 

@@ -22,6 +22,10 @@ from .w4a16_ref import (  # noqa: F401
     compare,
     compare_entries,
     pack_split,
+    silu,
+    swiglu,
+    swiglu_bound,
+    compare_swiglu,
     unpack_split,
     SLAB,
     STAGE_GROUPS,

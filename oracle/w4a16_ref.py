@@ -43,6 +43,12 @@ Readings taken where the pages are silent (each is listed in the design doc):
   layout from its index formula (64-row slabs, stages of 2 groups, zero code
   and zero scale as padding); it only moves bits, so the library's repack
   must match it byte for byte.
+* Fused gate/up SwiGLU (the pages' decode configuration is the gate+up matrix,
+  2 x 2048 rows; SwiGLU is the engine's MLP activation): W holds the gate rows
+  then the up rows; the result is silu(g) * u with silu(v) = v / (1 + e^-v),
+  evaluated in fp64 from the fp64 products.  Acceptance propagates the GEMM
+  bound of g and u through silu (|silu'| <= 1.1) and adds the rounding of an
+  fp32 evaluation of the epilogue (``compare_swiglu``).
 * Product: accumulated in fp64 (every fp32 x fp32 product is exact in fp64).
   An fp32 result is accepted iff |Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6
   elementwise, with w the dequantized fp32 weight and the sum in fp64.
@@ -276,6 +282,53 @@ def compare(Y: np.ndarray, X: np.ndarray, qweight: np.ndarray, scales: np.ndarra
     if np.shape(Y) != Yref.shape:
         raise ValueError(f"Y shape {np.shape(Y)} != {Yref.shape}")
     return _verdict(Y, Yref, T)
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """silu(v) = v / (1 + exp(-v)) in fp64 (exp overflow for very negative v gives -0)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """silu(X . gate^T) * (X . up^T) in fp64; W rows 0..F-1 gate, F..2F-1 up."""
+    Y = gemm(X, qweight, scales)
+    F = Y.shape[1] // 2
+    return silu(Y[:, :F]) * Y[:, F:]
+
+
+SILU_LIPSCHITZ = 1.1   # max |silu'(v)| = 1.0998...
+EPILOGUE_ULPS = 8      # fp32 exp, add, divide and multiply, rounded
+
+
+def swiglu_bound(X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Allowed |Y - swiglu| per output: the GEMM bound e_g, e_u of the gate and
+    up sums carried through silu(g) * u, plus the epilogue's fp32 rounding."""
+    Y = gemm(X, qweight, scales)
+    T = abs_gemm(X, qweight, scales)
+    F = Y.shape[1] // 2
+    g, u = Y[:, :F], Y[:, F:]
+    eg, eu = bound(T[:, :F]), bound(T[:, F:])
+    sg = np.abs(silu(g))
+    carried = SILU_LIPSCHITZ * eg * (np.abs(u) + eu) + sg * eu
+    rounding = EPILOGUE_ULPS * 2.0 ** -24 * (sg + SILU_LIPSCHITZ * eg) * (np.abs(u) + eu)
+    return carried + rounding
+
+
+def compare_swiglu(Y: np.ndarray, X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> dict:
+    """Elementwise check of a fused gate/up SwiGLU result against swiglu()."""
+    ref = swiglu(X, qweight, scales)
+    Y = np.asarray(Y, dtype=np.float64)
+    if Y.shape != ref.shape:
+        raise ValueError(f"shape {Y.shape} != {ref.shape}")
+    b = swiglu_bound(X, qweight, scales)
+    finite = bool(np.all(np.isfinite(Y)))
+    err = np.abs(Y - ref)
+    ratio = float(np.max(err / b)) if err.size else 0.0
+    return {"ok": finite and bool(np.all(err <= b)), "max_ratio": ratio,
+            "max_abs_err": float(err.max()) if err.size else 0.0, "finite": finite,
+            "n": int(err.size)}
 
 
 def compare_entries(Y: np.ndarray, X, qweight, scales, rows, cols) -> dict:

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
             "w4a16_abi_version", "w4a16_select_path", "w4a16_gemm_split",
             "w4a16_split_workspace_bytes", "w4a16_split_pack", "w4a16_split_pack_bytes",
-            "w4a16_gemm_split_packed"} <= set(names)
+            "w4a16_gemm_split_packed", "w4a16_gemm_swiglu"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     assert lib.w4a16_abi_version() == 1
@@ -211,6 +211,19 @@ def test_split_packed_gemm_errors(lib):
     assert g(X_, P_, Y_, k=48) == SHAPE
     assert g(X_, P_, Y_, group=16) == ARG
     assert g(None, None, None, ws=None, nb=0, m=0) == OK
+
+
+def test_swiglu_rejects_bad_arguments(lib):
+    sw = lambda x, q, s_, y, m, f, k, group=32: lib.w4a16_gemm_swiglu(x, q, s_, y, m, f, k, group, None)
+    assert sw(X_, Q_, S_, Y_, 1, 8, 48) == SHAPE
+    assert sw(X_, Q_, S_, Y_, 1, -1, 64) == ARG
+    assert sw(X_, Q_, S_, Y_, 1, 8, 64, group=16) == ARG
+    assert sw(None, Q_, S_, Y_, 1, 8, 64) == ARG
+    assert sw(X_ + 4, Q_, S_, Y_, 1, 8, 64) == ALIGN
+    assert sw(X_, Q_, S_, X_ + 64, 1, 8, 64) == ARG      # Y overlaps X
+    assert sw(X_, Q_, S_, Y_, 1, 1 << 30, 64) == SHAPE   # 2F above the row limit
+    assert sw(None, None, None, None, 0, 8, 64) == OK
+    assert sw(None, None, None, None, 3, 0, 64) == OK
 
 
 def test_binding_refuses_host_tensors(lib):
