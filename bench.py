@@ -49,8 +49,10 @@ CSRC = "int4_weight_only_03_amd/csrc/"
 PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5}
 SPLIT_PATHS = ("split", "packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
-PATH_SOURCES = {"gemv": ["gemv.hip"], "tile": ["tile.hip"], "split": ["split.hip"],
-                "packed": ["split.hip"], "swiglu": ["gemv.hip"]}
+PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
+                "split": ["split.hip"], "packed": ["split.hip"],
+                "swiglu": ["gemv.hip", "gemv_common.h"],
+                "grouped": ["grouped.hip", "gemv_common.h"]}
 
 
 def source_hash(path: str) -> str:
@@ -77,6 +79,121 @@ def measured_traffic(workload: str, path: str):
 def metric_in_gbs(wl) -> bool:
     """The metric is effective HBM GB/s for M <= 64 and TFLOP/s above."""
     return wl.M <= 64
+
+
+def time_steps(step, steps: int, stream):
+    """(ms per step of a graph replay of `steps` steps, eager per-launch ms, graphed)."""
+    import torch
+    # per-launch durations with events around each launch (eager), for the
+    # kernel-time cross-check against rocprofv3
+    n_ev = min(steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [a.elapsed_time(b) for a, b in evs]
+
+    graphed = True
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()                                  # warm replay
+        torch.cuda.synchronize()
+    except Exception as e:                          # capture refused: time eager launches
+        graphed = False
+        print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if graphed:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, per_launch_ms, graphed
+
+
+def gpu_leg_moe(name: str, steps: int, warmup: int):
+    """The grouped (MoE) GEMM on a synthetic routed decode batch."""
+    import torch
+    import int4_weight_only_03_amd as pkg
+
+    wl = workloads.MOE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    X, W, ti, off = workloads.make_moe(name)
+    packed = [pkg.w4a16_quantize(W[e]) for e in range(wl.E)]   # the library's host quantizer
+    qw = np.stack([q for q, _ in packed])
+    sc = np.stack([s for _, s in packed])
+    del packed
+    B = wl.algorithmic_bytes(off)
+    copies = max(1, -(-2 * MALL_BYTES // B))
+    Xd, Qd, Sd = (torch.from_numpy(a).to(dev) for a in (X, qw, sc))
+    Id, Od = torch.from_numpy(ti).to(dev), torch.from_numpy(off).to(dev)
+    sets = [(Xd.clone(), Qd.clone(), Sd.clone(),
+             torch.empty((wl.R, wl.N), dtype=torch.float32, device=dev)) for _ in range(copies)]
+    del Xd, Qd, Sd
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x, q, s, y = sets[i % copies]
+        pkg.w4a16_gemm_grouped(x, Id, Od, q, s, y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step, per_launch_ms, graphed = time_steps(step, steps, stream)
+    gbs = B / (ms_per_step * 1e-3) / 1e9
+    tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
+    roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name, "grouped")}
+    med = statistics.median(per_launch_ms)
+    active = int(np.count_nonzero(np.diff(off)))
+    extra = {"graph_replay": graphed, "rotation_copies": copies, "algorithmic_bytes": B,
+             "flops": wl.flops(), "per_launch_event_us_median": med * 1e3,
+             "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9, "path": "grouped",
+             "active_experts": active, "hbm_frac": gbs / HBM_PEAK_GBS,
+             "fp32_frac": tfs / FP32_PEAK_TFLOPS}
+    y0 = sets[0][3].cpu().numpy()
+    return gbs, "GB/s", ms_per_step, roof, extra, (X, qw, sc, ti, off, y0)
+
+
+def cpu_leg_moe(name: str, gpu_out, budget_s: float = 12.0):
+    """The oracle on a bounded sample of the grouped GEMM: the slots of the first experts."""
+    import oracle
+    wl = workloads.MOE_WORKLOADS[name]
+    X, qw, sc, ti, off, Y = gpu_out
+    cores = len(os.sched_getaffinity(0))
+    # sample: every slot of the first experts, up to 8 slots
+    e_end = 1
+    while e_end < wl.E and off[e_end + 1] <= 8:
+        e_end += 1
+    r_end = int(off[e_end])
+    sub_off = off[:e_end + 1]
+    times, Yref = [], None
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        Yref = oracle.grouped_gemm(X, ti[:r_end], sub_off, qw[:e_end], sc[:e_end])
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    t = statistics.median(times)
+    active = int(np.count_nonzero(np.diff(sub_off)))
+    sample_bytes = active * (wl.N * wl.K // 2 + 4 * wl.N * (wl.K // 32)) + 4 * r_end * (wl.K + wl.N)
+    v = oracle.compare_grouped(Y[:r_end], X, ti[:r_end], sub_off, qw[:e_end], sc[:e_end])
+    return {"value": sample_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"slots 0..{r_end - 1} (experts 0..{e_end - 1}, {active} active), "
+                      f"median of {len(times)} runs, {t * 1e3:.1f} ms each",
+            "gpu_parity_on_sample_max_err_over_bound": v["max_ratio"]}
 
 
 def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
@@ -140,43 +257,7 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         step(i)
     torch.cuda.synchronize()
 
-    # per-launch durations with events around each launch (eager), for the
-    # kernel-time cross-check against rocprofv3
-    n_ev = min(steps, 200)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_launch_ms = [a.elapsed_time(b) for a, b in evs]
-
-    graphed = True
-    try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                step(i)
-        g.replay()                                  # warm replay
-        torch.cuda.synchronize()
-    except Exception as e:                          # capture refused: time eager launches
-        graphed = False
-        print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    if graphed:
-        g.replay()
-    else:
-        for i in range(steps):
-            step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / steps
+    ms_per_step, per_launch_ms, graphed = time_steps(step, steps, stream)
 
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
@@ -286,9 +367,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_gate_up",
-                    help="comma-separated names from %s, or 'all'" % ", ".join(workloads.ORDER))
+                    help="comma-separated names from %s, or 'all'" % ", ".join(
+                        workloads.ORDER + list(workloads.MOE_WORKLOADS)))
     ap.add_argument("--path", default="auto",
-                    help="kernel path(s), comma-separated: auto, gemv, tile, split")
+                    help="kernel path(s), comma-separated: auto, gemv, tile, split, packed, "
+                         "swiglu (grouped-MoE workloads always run the grouped kernel)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -300,11 +383,16 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    names = workloads.ORDER if args.workload == "all" else args.workload.split(",")
+    names = (workloads.ORDER + list(workloads.MOE_WORKLOADS) if args.workload == "all"
+             else args.workload.split(","))
     paths = args.path.split(",")
     for p in paths:
         if p not in PATH_NAMES:
             ap.error(f"unknown path {p!r}")
+    for name in names:
+        if name in workloads.MOE_WORKLOADS:
+            run_moe(name, args)
+    names = [n for n in names if n not in workloads.MOE_WORKLOADS]
     for name, path in [(n, p) for n in names for p in paths]:
         wl = workloads.WORKLOADS[name]
         steps = args.steps if wl.M < 1024 else max(5, min(args.steps, 20))
@@ -326,6 +414,25 @@ def main():
         if not args.no_cpu:
             line["cpu_baseline"] = cpu_leg(name, out, path=path)
         print(json.dumps(line), flush=True)
+
+
+def run_moe(name, args):
+    wl = workloads.MOE_WORKLOADS[name]
+    print(f"# {name}: T={wl.T} E={wl.E} top-{wl.topk} K={wl.K} N={wl.N} steps={args.steps} "
+          f"path=grouped", file=sys.stderr, flush=True)
+    value, unit, ms, roof, extra, out = gpu_leg_moe(name, args.steps, args.warmup)
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "T": wl.T, "experts": wl.E, "topk": wl.topk, "K": wl.K,
+                   "N": wl.N, "group": 32, "note": wl.note, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    line.update(extra)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_leg_moe(name, out)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -121,6 +121,30 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
 int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scales, float *Y,
                       int64_t M, int64_t F, int64_t K, int32_t group, void *stream);
 
+/*
+ * Grouped (mixture-of-experts) W4A16 GEMM in one launch: many experts, each
+ * applied to its own, possibly empty, set of token rows -- the pages run the
+ * MoE experts through the INT4 path and plan a MoE kernel for production.
+ *   X              float [T][K]        tokens
+ *   token_index    int32 [R]           routed slot r reads token token_index[r]
+ *   expert_offsets int32 [E+1]         expert e owns slots [offsets[e], offsets[e+1]):
+ *                                      non-decreasing, offsets[0] = 0, offsets[E] = R
+ *   qweight        int32 [E][N][K/8]   expert e's weights, layout as w4a16_gemm
+ *   scales         float [E][N][K/32]
+ *   Y              float [R][N]        Y[r] = X[token_index[r]] . dequant(W_e)^T, e
+ *                                      the expert owning slot r
+ * All DEVICE memory.  The same arithmetic and tolerance as w4a16_gemm.  An
+ * expert with no slot costs one empty workgroup and its weights are not
+ * read.  token_index and expert_offsets are read on the device and clamped
+ * into range (malformed routing gives wrong values, never an out-of-bounds
+ * access).  R == 0 or N == 0 is a no-op; T == 0 with R > 0, E < 1 or
+ * E > 65535 is an error; otherwise errors as w4a16_gemm (Y overlapping any
+ * input is W4A16_ERR_ARG; token_index and expert_offsets 4-byte aligned).
+ */
+int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t *expert_offsets,
+                       const int32_t *qweight, const float *scales, float *Y, int64_t T,
+                       int64_t R, int64_t E, int64_t N, int64_t K, int32_t group, void *stream);
+
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 

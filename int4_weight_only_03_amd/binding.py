@@ -54,6 +54,9 @@ _SIGS = {
     "w4a16_gemm_swiglu": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                            ctypes.c_void_p], ctypes.c_int),
+    "w4a16_gemm_grouped": ([ctypes.c_void_p] * 6 + [ctypes.c_int64] * 5 + [ctypes.c_int32,
+                                                                      ctypes.c_void_p],
+                           ctypes.c_int),
     "w4a16_split_pack_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
     "w4a16_split_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
@@ -222,6 +225,37 @@ def w4a16_gemm_swiglu(X, qweight, scales, Y=None, stream=None):
                                   Y.data_ptr(), M, F, K, GROUP, _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_swiglu")
+    return Y
+
+
+def w4a16_gemm_grouped(X, token_index, expert_offsets, qweight, scales, Y=None, stream=None):
+    """Grouped MoE GEMM: Y[r] = X[token_index[r]] . dequant(W_e)^T for the expert e
+    owning slot r; qweight [E][N][K/8], scales [E][N][K/32], offsets [E+1]."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    token_index = _dev(token_index, torch.int32, "token_index")
+    expert_offsets = _dev(expert_offsets, torch.int32, "expert_offsets")
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    if X.dim() != 2 or qweight.dim() != 3 or scales.dim() != 3:
+        raise ValueError("X must be 2-D, qweight and scales 3-D [E][N][...]")
+    T, K = X.shape
+    E, N, K8 = qweight.shape
+    R = token_index.numel()
+    if K8 * 8 != K or tuple(scales.shape) != (E, N, K // GROUP) or expert_offsets.numel() != E + 1:
+        raise ValueError("shapes disagree")
+    if Y is None:
+        Y = torch.empty((R, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (R, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(R, N)}")
+    st = load().w4a16_gemm_grouped(X.data_ptr(), token_index.data_ptr(),
+                                   expert_offsets.data_ptr(), qweight.data_ptr(),
+                                   scales.data_ptr(), Y.data_ptr(), T, R, E, N, K, GROUP,
+                                   _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_grouped")
     return Y
 
 

@@ -99,6 +99,33 @@ int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scale
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t *expert_offsets,
+                       const int32_t *qweight, const float *scales, float *Y, int64_t T,
+                       int64_t R, int64_t E, int64_t N, int64_t K, int32_t group, void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (T < 0 || R < 0 || E <= 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)
+    return W4A16_ERR_SHAPE;
+  if (R == 0 || N == 0) return W4A16_OK;
+  if (T == 0) return W4A16_ERR_ARG;  // slots but no tokens to read
+  if (!X || !token_index || !expert_offsets || !qweight || !scales || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(qweight, 16) || !aligned(scales, 4) || !aligned(Y, 4) ||
+      !aligned(token_index, 4) || !aligned(expert_offsets, 4))
+    return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(T) * size_t(K) * 4, by = size_t(R) * size_t(N) * 4;
+  const size_t bq = size_t(E) * size_t(N) * size_t(K) / 2;
+  const size_t bs = size_t(E) * size_t(N) * size_t(K / W4A16_GROUP) * 4;
+  const size_t bi = size_t(R) * 4, bo = size_t(E + 1) * 4;
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, qweight, bq) || overlaps(Y, by, scales, bs) ||
+      overlaps(Y, by, token_index, bi) || overlaps(Y, by, expert_offsets, bo))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_grouped(X, token_index, expert_offsets, qweight, scales, Y,
+                                       int(T), int(R), int(E), int(N), int(K),
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;

@@ -44,6 +44,12 @@ hipError_t launch_split_with(const float *X, const void *weights, const float *s
 hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const float *scales,
                               float *Y, int M, int F, int K, hipStream_t stream);
 
+// Grouped (MoE) GEMM: Y[r] = X[token_index[r]] . dequant(W_e)^T for the
+// expert e whose slot range [offsets[e], offsets[e+1]) holds r.
+hipError_t launch_grouped(const float *X, const int32_t *token_index, const int32_t *offsets,
+                          const int32_t *qweight, const float *scales, float *Y, int T, int R,
+                          int E, int N, int K, hipStream_t stream);
+
 // Largest M the GEMV path is chosen for by default.
 constexpr int kGemvMaxM = 4;
 

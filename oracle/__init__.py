@@ -23,6 +23,9 @@ from .w4a16_ref import (  # noqa: F401
     compare_entries,
     pack_split,
     silu,
+    check_routing,
+    grouped_gemm,
+    compare_grouped,
     swiglu,
     swiglu_bound,
     compare_swiglu,

@@ -43,6 +43,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
   layout from its index formula (64-row slabs, stages of 2 groups, zero code
   and zero scale as padding); it only moves bits, so the library's repack
   must match it byte for byte.
+* Grouped (MoE) GEMM: routed slot r of expert e is the product of token
+  token_index[r] with expert e's weights (the pages run the MoE experts
+  through the INT4 path); ``grouped_gemm`` applies ``gemm`` expert by expert
+  to the gathered token rows, and the tolerance is that of ``gemm``.
 * Fused gate/up SwiGLU (the pages' decode configuration is the gate+up matrix,
   2 x 2048 rows; SwiGLU is the engine's MLP activation): W holds the gate rows
   then the up rows; the result is silu(g) * u with silu(v) = v / (1 + e^-v),
@@ -282,6 +286,44 @@ def compare(Y: np.ndarray, X: np.ndarray, qweight: np.ndarray, scales: np.ndarra
     if np.shape(Y) != Yref.shape:
         raise ValueError(f"Y shape {np.shape(Y)} != {Yref.shape}")
     return _verdict(Y, Yref, T)
+
+
+def check_routing(token_index: np.ndarray, offsets: np.ndarray, T: int, E: int) -> None:
+    """Routing must be well formed: offsets non-decreasing from 0 to R, token
+    indices in [0, T)."""
+    token_index = np.asarray(token_index)
+    offsets = np.asarray(offsets)
+    R = token_index.size
+    if offsets.shape != (E + 1,) or offsets[0] != 0 or offsets[-1] != R:
+        raise ValueError("expert offsets must run from 0 to R with E + 1 entries")
+    if np.any(np.diff(offsets) < 0):
+        raise ValueError("expert offsets must be non-decreasing")
+    if R and (token_index.min() < 0 or token_index.max() >= T):
+        raise ValueError("token index out of range")
+
+
+def grouped_gemm(X, token_index, offsets, qweight, scales) -> np.ndarray:
+    """Y[r] = X[token_index[r]] . dequant(W_e)^T for the expert e owning slot r (fp64)."""
+    E, N = qweight.shape[0], qweight.shape[1]
+    check_routing(token_index, offsets, X.shape[0], E)
+    Y = np.zeros((len(token_index), N))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            Y[r0:r1] = gemm(X[token_index[r0:r1]], qweight[e], scales[e])
+    return Y
+
+
+def compare_grouped(Y, X, token_index, offsets, qweight, scales) -> dict:
+    """Elementwise check of a grouped result: each expert's rows against gemm."""
+    ref = grouped_gemm(X, token_index, offsets, qweight, scales)
+    Y = np.asarray(Y, dtype=np.float64)
+    T = np.zeros_like(ref)
+    for e in range(qweight.shape[0]):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            T[r0:r1] = abs_gemm(X[token_index[r0:r1]], qweight[e], scales[e])
+    return _verdict(Y, ref, T)
 
 
 def silu(v: np.ndarray) -> np.ndarray:

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
             "w4a16_abi_version", "w4a16_select_path", "w4a16_gemm_split",
             "w4a16_split_workspace_bytes", "w4a16_split_pack", "w4a16_split_pack_bytes",
-            "w4a16_gemm_split_packed", "w4a16_gemm_swiglu"} <= set(names)
+            "w4a16_gemm_split_packed", "w4a16_gemm_swiglu", "w4a16_gemm_grouped"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     assert lib.w4a16_abi_version() == 1
@@ -224,6 +224,26 @@ def test_swiglu_rejects_bad_arguments(lib):
     assert sw(X_, Q_, S_, Y_, 1, 1 << 30, 64) == SHAPE   # 2F above the row limit
     assert sw(None, None, None, None, 0, 8, 64) == OK
     assert sw(None, None, None, None, 3, 0, 64) == OK
+
+
+def test_grouped_rejects_bad_arguments(lib):
+    I_, O_ = BASE + (6 << 32), BASE + (7 << 32)  # fake token_index, expert_offsets
+    gr = lambda x, ti, off, q, s_, y, T, R, E, N, K, group=32: lib.w4a16_gemm_grouped(
+        x, ti, off, q, s_, y, T, R, E, N, K, group, None)
+    assert gr(X_, I_, O_, Q_, S_, Y_, 4, 8, 3, 16, 48) == SHAPE
+    assert gr(X_, I_, O_, Q_, S_, Y_, 4, 8, 0, 16, 64) == ARG        # no experts
+    assert gr(X_, I_, O_, Q_, S_, Y_, 4, 8, 70000, 16, 64) == SHAPE  # too many experts
+    assert gr(X_, I_, O_, Q_, S_, Y_, 0, 8, 3, 16, 64) == ARG        # slots, no tokens
+    assert gr(X_, I_, O_, Q_, S_, Y_, 4, -1, 3, 16, 64) == ARG
+    assert gr(X_, None, O_, Q_, S_, Y_, 4, 8, 3, 16, 64) == ARG
+    assert gr(X_, I_, None, Q_, S_, Y_, 4, 8, 3, 16, 64) == ARG
+    assert gr(X_ + 4, I_, O_, Q_, S_, Y_, 4, 8, 3, 16, 64) == ALIGN
+    assert gr(X_, I_ + 2, O_, Q_, S_, Y_, 4, 8, 3, 16, 64) == ALIGN
+    assert gr(X_, I_, O_, Q_, S_, X_ + 64, 4, 8, 3, 16, 64) == ARG   # Y overlaps X
+    assert gr(X_, I_, O_, Q_, S_, I_, 4, 8, 3, 16, 64) == ARG         # Y overlaps token_index
+    assert gr(X_, I_, O_, Q_, S_, Y_, 4, 8, 3, 16, 64, group=16) == ARG
+    assert gr(None, None, None, None, None, None, 0, 0, 3, 16, 64) == OK   # no slots
+    assert gr(None, None, None, None, None, None, 4, 8, 3, 0, 64) == OK    # N == 0
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -65,6 +65,72 @@ WORKLOADS = {
 ORDER = ["tiny", "decode_gate_up", "decode_down", "verify_tree", "prefill"]
 
 
+@dataclass(frozen=True)
+class MoeWorkload:
+    """Grouped (MoE) GEMM: T tokens, each routed to `topk` of E experts with
+    uniform random routing; every expert has its own N x K weights."""
+    name: str
+    T: int
+    E: int
+    topk: int
+    N: int
+    K: int
+    seed: int
+    note: str
+
+    @property
+    def R(self) -> int:
+        return self.T * self.topk
+
+    def algorithmic_bytes(self, offsets: np.ndarray) -> int:
+        """Weights and scales of every expert with at least one slot, the token
+        rows and the output rows, each moved once."""
+        active = int(np.count_nonzero(np.diff(offsets)))
+        N, K = self.N, self.K
+        return active * (N * K // 2 + 4 * N * (K // GROUP)) + 4 * self.T * K + 4 * self.R * N
+
+    def flops(self) -> int:
+        return 2 * self.R * self.N * self.K
+
+
+MOE_WORKLOADS = {
+    "moe_decode": MoeWorkload("moe_decode", 16, 32, 4, 1024, 7168, 5,
+                              "decode batch of 16 tokens, top-4 of 32 experts (some empty), "
+                              "N=1024 per expert"),
+}
+
+
+def moe_routing(rng: np.random.Generator, T: int, E: int, topk: int):
+    """Uniform top-k routing: each token draws topk distinct experts.  Returns
+    (token_index int32 [T*topk], expert_offsets int32 [E+1]): slots sorted by
+    expert (then token), expert e owning slots offsets[e]..offsets[e+1]-1."""
+    choice = np.stack([rng.permutation(E)[:topk] for _ in range(T)])   # [T][topk]
+    expert = choice.reshape(-1)
+    token = np.repeat(np.arange(T), topk)
+    order = np.lexsort((token, expert))
+    counts = np.bincount(expert, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    return token[order].astype(np.int32), offsets.astype(np.int32)
+
+
+def moe_case(T: int, E: int, topk: int, N: int, K: int, seed: int):
+    """(X [T][K], W [E][N][K], token_index [R], expert_offsets [E+1]).
+    Draw order: X, then each expert's W in turn, then the routing."""
+    rng = np.random.default_rng(seed)
+    X = _draw_x(rng, "gauss", T, K)
+    W = np.empty((E, N, K), dtype=np.float32)
+    for e in range(E):
+        W[e] = _draw_w(rng, "gauss", N, K)
+    token_index, offsets = moe_routing(rng, T, E, topk)
+    return X, W, token_index, offsets
+
+
+def make_moe(name: str):
+    wl = MOE_WORKLOADS[name]
+    return moe_case(wl.T, wl.E, wl.topk, wl.N, wl.K, wl.seed)
+
+
 def _draw_x(rng: np.random.Generator, kind: str, M: int, K: int) -> np.ndarray:
     if kind == "gauss":
         x = rng.standard_normal((M, K))
