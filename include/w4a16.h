@@ -59,6 +59,8 @@ extern "C" {
                                  4-byte aligned */
 #define W4A16_ERR_NONFINITE 4 /* w4a16_quantize: a weight is NaN or infinite */
 #define W4A16_ERR_HIP 5       /* the HIP runtime refused a launch */
+#define W4A16_ERR_IO 6        /* w4a16_load_quantized / w4a16_save_quantized: a file cannot be
+                                 opened, read or written, or its size is not the expected one */
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
@@ -214,6 +216,38 @@ int w4a16_split_pack(const int32_t *qweight, const float *scales, int64_t N, int
 int w4a16_gemm_split_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
                             int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * Raw weight files of one quantized weight W[N][K], as the pages' INT4 model
+ * bundles store them: "<name>.qw" holds qweight[N][K/8] as little-endian int32
+ * and "<name>.sc" holds scales[N][K/32] as little-endian fp32, both row-major
+ * with no header; the group size (32) is metadata kept apart from the files,
+ * and a weight with a .qw file runs through W4A16 while the others stay fp32
+ * ("The Quiet Commit: How a Single Documentation Edit Marks the Completion of
+ * a Major Engineering Milestone", section "The INT4 Milestone: From FP32 to
+ * Production-Ready Quantization").  The files carry no shape, so the caller
+ * passes N and K; each file must be exactly N*K/2 (.qw) and N*K/8 (.sc) bytes.
+ *
+ * w4a16_load_quantized reads both files into HOST buffers the caller owns
+ * (qweight: N*K/8 int32, scales: N*K/32 float).  Synchronous; no GPU use.
+ * Returns W4A16_ERR_IO if a file cannot be opened or read or has another size
+ * (both sizes are checked before anything is read; on any error the buffers'
+ * contents are unspecified), W4A16_ERR_NONFINITE if a scale is NaN or
+ * infinite (the quantizer writes none), W4A16_ERR_ARG on NULL
+ * paths or buffers, negative extents, K == 0 or group != 32, W4A16_ERR_SHAPE
+ * if K % 32 != 0 or an extent exceeds its W4A16_MAX_*.  N == 0 reads two empty
+ * files.
+ */
+int w4a16_load_quantized(const char *qw_path, const char *sc_path, int64_t N, int64_t K,
+                         int32_t group, int32_t *qweight, float *scales);
+
+/*
+ * Write qweight[N][K/8] and scales[N][K/32] (HOST memory) to the two raw files
+ * above, replacing any existing files.  Synchronous.  Errors as
+ * w4a16_load_quantized (W4A16_ERR_IO when a file cannot be written).
+ */
+int w4a16_save_quantized(const char *qw_path, const char *sc_path, int64_t N, int64_t K,
+                         int32_t group, const int32_t *qweight, const float *scales);
 
 #ifdef __cplusplus
 }

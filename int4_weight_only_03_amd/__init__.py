@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     w4a16_gemm_split,
     w4a16_gemm_swiglu,
     w4a16_gemm_split_packed,
+    w4a16_load_quantized,
+    w4a16_save_quantized,
     w4a16_split_pack,
     w4a16_split_pack_bytes,
     w4a16_split_workspace_bytes,
@@ -22,3 +24,4 @@ from .binding import (  # noqa: F401
     w4a16_select_path,
     w4a16_status_str,
 )
+from .bundle import WeightBundle  # noqa: F401,E402

@@ -65,6 +65,10 @@ _SIGS = {
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
                                 ctypes.c_int),
+    "w4a16_load_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
+                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_save_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
+                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
 
 
@@ -118,6 +122,33 @@ def w4a16_quantize(W: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_quantize")
     return qw, sc
+
+
+def w4a16_load_quantized(qw_path, sc_path, N: int, K: int) -> tuple[np.ndarray, np.ndarray]:
+    """Read raw `.qw` / `.sc` files of an N x K weight into host arrays
+    (qweight int32 [N][K/8], scales fp32 [N][K/32])."""
+    qw = np.empty((N, max(K // 8, 0)), dtype=np.int32)
+    sc = np.empty((N, max(K // GROUP, 0)), dtype=np.float32)
+    st = load().w4a16_load_quantized(os.fsencode(qw_path), os.fsencode(sc_path), N, K, GROUP,
+                                     qw.ctypes.data, sc.ctypes.data)
+    if st != W4A16_OK:
+        raise W4A16Error(st, f"w4a16_load_quantized({qw_path}, {sc_path})")
+    return qw, sc
+
+
+def w4a16_save_quantized(qw_path, sc_path, qweight: np.ndarray, scales: np.ndarray) -> None:
+    """Write host qweight [N][K/8] int32 and scales [N][K/32] fp32 as raw `.qw` / `.sc` files."""
+    qweight = np.ascontiguousarray(qweight)
+    scales = np.ascontiguousarray(scales)
+    if qweight.dtype != np.int32 or scales.dtype != np.float32 or qweight.ndim != 2:
+        raise TypeError("qweight must be 2-D int32 and scales float32")
+    N, K = qweight.shape[0], 8 * qweight.shape[1]
+    if scales.shape != (N, K // GROUP):
+        raise ValueError(f"scales shape {scales.shape} != {(N, K // GROUP)}")
+    st = load().w4a16_save_quantized(os.fsencode(qw_path), os.fsencode(sc_path), N, K, GROUP,
+                                     qweight.ctypes.data, scales.ctypes.data)
+    if st != W4A16_OK:
+        raise W4A16Error(st, f"w4a16_save_quantized({qw_path}, {sc_path})")
 
 
 def _dev(t, dtype, name):

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libw4a16.so")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["gemv.hip", "tile.hip", "split.hip", "grouped.hip"]
-HOST_SOURCES = ["w4a16_api.cpp"]
+HOST_SOURCES = ["w4a16_api.cpp", "w4a16_io.cpp"]
 # per-source options: the split path's MFMA results stay in VGPRs (the scale
 # FMAs read them directly, no accumulator-register copies)
 EXTRA = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

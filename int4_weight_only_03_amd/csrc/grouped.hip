@@ -138,6 +138,12 @@ constexpr int kRowsMaxLds = 64 * 1024;  // staged token rows, bytes
 constexpr int kGL = 4;                   // groups per lane per pass (64 * kGL groups)
 constexpr int kStage = 8;                // 16-byte staging loads per thread in flight
 
+// Staged rows keep each group's eight float4 together but rotate their order
+// by the group index (slot v of group g at v ^ (g % 8)): a lane reads one
+// group, so the lanes of one read would otherwise all sit 128 bytes apart on
+// the same LDS banks.
+__device__ __forceinline__ int x_slot(int q) { return (q & ~7) | ((q ^ (q >> 3)) & 7); }
+
 template <int MT, int RB>
 __global__ void __launch_bounds__(kRowsThreads)
 grouped_rows(const float *__restrict__ X, const int32_t *__restrict__ token_index,
@@ -178,8 +184,10 @@ grouped_rows(const float *__restrict__ X, const int32_t *__restrict__ token_inde
 #pragma unroll
         for (int u = 0; u < kStage; ++u) v[u] = xrow[m][std::min(k0 + u * kRowsThreads, K4 - 1)];
 #pragma unroll
-        for (int u = 0; u < kStage; ++u)
-          if (k0 + u * kRowsThreads < K4) xs4[m * K4 + k0 + u * kRowsThreads] = v[u];
+        for (int u = 0; u < kStage; ++u) {
+          const int q = k0 + u * kRowsThreads;  // float4 q of the row: group q/8, slot q%8
+          if (q < K4) xs4[m * K4 + x_slot(q)] = v[u];
+        }
       }
     __syncthreads();
     for (int n0 = n_begin + wave * RB; n0 < n_end; n0 += 4 * RB) {
@@ -211,7 +219,7 @@ grouped_rows(const float *__restrict__ X, const int32_t *__restrict__ token_inde
             const float4 *xp = reinterpret_cast<const float4 *>(xs + m * K + long(gc) * kGroup);
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
-              const float4 f = xp[v];
+              const float4 f = xp[v ^ (gc & 7)];
               x[m][4 * v + 0] = f.x;
               x[m][4 * v + 1] = f.y;
               x[m][4 * v + 2] = f.z;

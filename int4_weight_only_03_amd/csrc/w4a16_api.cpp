@@ -60,6 +60,7 @@ const char *w4a16_status_str(int status) {
     case W4A16_ERR_ALIGN: return "misaligned pointer (X, qweight: 16 bytes; scales, Y: 4 bytes)";
     case W4A16_ERR_NONFINITE: return "non-finite weight";
     case W4A16_ERR_HIP: return "HIP runtime error";
+    case W4A16_ERR_IO: return "weight file cannot be read or written, or has the wrong size";
     default: return "unknown status";
   }
 }
