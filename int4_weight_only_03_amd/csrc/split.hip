@@ -36,6 +36,7 @@
 //    order (deterministic), undoes the row's power of two and stores Y.
 
 #include "w4a16_internal.h"
+#include "limbs.h"
 
 #include <algorithm>
 #include <cmath>
@@ -43,9 +44,6 @@
 namespace w4a16 {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 64;      // rows of X / Y per workgroup tile
@@ -60,29 +58,6 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-// exponent e with max|x| * 2^e in [2^14, 2^15); 0 for a zero or non-finite max
-__device__ __forceinline__ int row_exponent(float mx) {
-  int e = 0;
-  if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
-    int E;
-    frexpf(mx, &E);  // mx in [2^(E-1), 2^E)
-    e = 15 - E;
-  }
-  return e;
-}
-
-__device__ __forceinline__ void split_block(const float4 a, const float4 c, int e, half8_t &h,
-                                            half8_t &l) {
-  const float v[8] = {a.x, c.x, a.y, c.y, a.z, c.z, a.w, c.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float xs = ldexpf(v[i], e);
-    const _Float16 hv = (_Float16)xs;
-    h[i] = hv;
-    l[i] = (_Float16)(xs - (float)hv);
-  }
 }
 
 // kInRegs: K <= 8 * 256 * kPrepRegBlocks, the row is read once and kept in
@@ -147,26 +122,6 @@ split_prep(const float *__restrict__ X, _Float16 *__restrict__ xl, int *__restri
 
 // ---------------------------------------------------------------- GEMM
 
-// f16 (q - 8) pairs from one word of 8 nibbles: VGPR p holds nibbles p, p+4.
-// (w & mask) | 0x6400 puts a nibble into the mantissa of 1024 (v_bitop3).
-__device__ __forceinline__ half8_t nibbles_to_f16(uint32_t w) {
-  const uint32_t t = w >> 8;
-  const half2_t p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64006400u, 0xEA));
-  const half2_t p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64006400u, 0xEA));
-  const half2_t p2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(t, 0x000F000Fu, 0x64006400u, 0xEA));
-  const half2_t p3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(t, 0x00F000F0u, 0x64006400u, 0xEA));
-  const half2_t c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const half2_t c72 = {(_Float16)72.0f, (_Float16)72.0f};
-  const half2_t c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2_t r0 = p0 - c1032;       // (1024 + q) - 1032
-  const half2_t r1 = p1 * c16 - c72;   // (1024 + 16q) / 16 - 72
-  const half2_t r2 = p2 - c1032;
-  const half2_t r3 = p3 * c16 - c72;
-  half8_t o;
-  o[0] = r0[0]; o[1] = r0[1]; o[2] = r1[0]; o[3] = r1[1];
-  o[4] = r2[0]; o[5] = r2[1]; o[6] = r3[0]; o[7] = r3[1];
-  return o;
-}
 
 // Work moves in stages of 2 groups (64 k).  A stage's operands are copied
 // straight from global memory into LDS (global_load_lds), D stages deep, so
@@ -540,7 +495,11 @@ split_pack(const uint32_t *__restrict__ qw, const float *__restrict__ sc, uint4 
 }
 
 // Y = 2^-e(m) * (sum over splits in order of the partials): one float4 of
-// outputs per thread when N % 4 == 0, else one output.
+// outputs per thread when N % 4 == 0, else one output.  The partials' loads
+// go out kBatch at a time before any of them is added (the adds stay in split
+// order, so the result does not depend on the batching).
+constexpr int kReduceBatch = 8;
+
 template <bool kVec4>
 __global__ void __launch_bounds__(256)
 split_reduce(const float *__restrict__ partial, const int *__restrict__ rexp,
@@ -549,21 +508,42 @@ split_reduce(const float *__restrict__ partial, const int *__restrict__ rexp,
   const long i = long(blockIdx.x) * 256 + threadIdx.x;
   if constexpr (kVec4) {
     if (4 * i >= total) return;
-    float4 v = reinterpret_cast<const float4 *>(partial)[i];
-    for (int z = 1; z < S; ++z) {
-      const float4 p = reinterpret_cast<const float4 *>(partial + long(z) * total)[i];
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
+    const float4 *p4 = reinterpret_cast<const float4 *>(partial);
+    const long stride = total / 4;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int z0 = 0; z0 < S; z0 += kReduceBatch) {
+      float4 p[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (z0 + u < S) p[u] = p4[long(z0 + u) * stride + i];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (z0 + u < S) {
+          if (z0 + u == 0) {
+            v = p[u];
+          } else {
+            v.x += p[u].x;
+            v.y += p[u].y;
+            v.z += p[u].z;
+            v.w += p[u].w;
+          }
+        }
     }
     const int e = rexp[(4 * i) / N];
     reinterpret_cast<float4 *>(Y)[i] =
         make_float4(ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e));
   } else {
     if (i >= total) return;
-    float v = partial[i];
-    for (int z = 1; z < S; ++z) v += partial[long(z) * total + i];
+    float v = 0.0f;
+    for (int z0 = 0; z0 < S; z0 += kReduceBatch) {
+      float p[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (z0 + u < S) p[u] = partial[long(z0 + u) * total + i];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (z0 + u < S) v = z0 + u == 0 ? p[u] : v + p[u];
+    }
     Y[i] = ldexpf(v, -rexp[i / N]);
   }
 }

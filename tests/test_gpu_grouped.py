@@ -51,6 +51,8 @@ def run(X, ti, off, q, s, dev, Y=None):
     (32, 4, 2, 96, 512),      # ~16 slots per expert (4-row chunks)
     (9, 3, 2, 257, 2048),     # 2-row chunks
     (4, 8, 8, 128, 7168),     # every expert used, K of the gate+up width
+    (3, 4, 2, 100, 288),      # 1.5 slots per expert: 2-row chunks on the matrix cores
+    (6, 4, 2, 48, 16384 + 32),  # K too long for 4 staged rows: fewer rows per chunk
 ])
 def test_grouped_shapes(dev, T, E, topk, N, K):
     say(f"grouped T={T} E={E} topk={topk} N={N} K={K}")
