@@ -306,6 +306,21 @@ __host__ __device__ constexpr int mfma_lds_bytes(int MR, int G4) {
   return 2 * mfma_region_bytes(MR, G4) + kMfmaWaves * MR * 4;
 }
 
+// LDS writes of this wave complete, then the workgroup barrier; the wave's
+// global loads stay in flight
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// max |x| over one 8-wide block held as two float4
+__device__ __forceinline__ float block_absmax(float4 a, float4 c) {
+  return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+               fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+}
+
 // one 4-group step of weights (lane (c, R): group 4*step + R of its row) and
 // the 4 scales of its row
 template <bool kSc4>
@@ -413,7 +428,7 @@ __device__ __forceinline__ void mfma_stream(const unsigned char *__restrict__ xa
 
 // one chunk of MC (<= MR) slots: row maxima, then per window of W groups the
 // limb split and the stream.  Rows past MC of the tile read the zero chunk.
-template <int MR, int MC, bool kSc4>
+template <int MR, int MC, bool kSc4, bool kOnePass>
 __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
                                            const int32_t *__restrict__ token_index,
                                            unsigned char *__restrict__ xa, float *__restrict__ red,
@@ -432,52 +447,67 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
   const int R_ = lane >> 4;
   constexpr int PD = kMfmaDepth<kSc4>;
 
-  // the chunk's first weight loads go out first: they do not depend on the
-  // activations
-  uint4 w[PD];
-  float4 s[PD];
-  if (n0 < N) {
-#pragma unroll
-    for (int p = 0; p < PD; ++p) mfma_load<kSc4>(wrow, srow, G, std::min(p, S - 1), R_, w[p], s[p]);
-  }
   long xrow[MC];  // float4 offset of each slot's token row
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
     const int tok = token_index[rbase + r];
     xrow[r] = long(std::min(std::max(tok, 0), T - 1)) * K4;
   }
-
-  // row maxima (two 8-wide blocks per row and thread in flight)
-  float mx[MC];
-#pragma unroll
-  for (int r = 0; r < MC; ++r) mx[r] = 0.0f;
-  for (int j0 = t; j0 < K8; j0 += 2 * kMfmaThreads) {
-    float4 a[MC][2], c[MC][2];
+  // kOnePass (4 G4 <= 2 kMfmaThreads 8-wide blocks per row): the token rows
+  // are read once, before the weights, and kept in registers for the split
+  float4 a[MC][2], c[MC][2];
+  if constexpr (kOnePass) {
 #pragma unroll
     for (int r = 0; r < MC; ++r)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const long j = std::min(j0 + u * kMfmaThreads, K8 - 1);
+        const long j = std::min(t + u * kMfmaThreads, K8 - 1);
         a[r][u] = X4[xrow[r] + 2 * j];
         c[r][u] = X4[xrow[r] + 2 * j + 1];
       }
+  }
+  // the ring's first weight loads: they do not depend on the activations
+  // (waves past N load clamped rows and compute with them, but store nothing)
+  uint4 w[PD];
+  float4 s[PD];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) mfma_load<kSc4>(wrow, srow, G, std::min(p, S - 1), R_, w[p], s[p]);
+
+  // row maxima
+  float mx[MC];
+#pragma unroll
+  for (int r = 0; r < MC; ++r) mx[r] = 0.0f;
+  if constexpr (kOnePass) {
 #pragma unroll
     for (int r = 0; r < MC; ++r)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        mx[r] = fmaxf(mx[r], fmaxf(fmaxf(fmaxf(fabsf(a[r][u].x), fabsf(a[r][u].y)),
-                                         fmaxf(fabsf(a[r][u].z), fabsf(a[r][u].w))),
-                                   fmaxf(fmaxf(fabsf(c[r][u].x), fabsf(c[r][u].y)),
-                                         fmaxf(fabsf(c[r][u].z), fabsf(c[r][u].w)))));
+        mx[r] = fmaxf(mx[r], block_absmax(a[r][u], c[r][u]));
+  } else {
+    for (int j0 = t; j0 < K8; j0 += 2 * kMfmaThreads) {
+      float4 a2[MC][2], c2[MC][2];
+#pragma unroll
+      for (int r = 0; r < MC; ++r)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const long j = std::min(j0 + u * kMfmaThreads, K8 - 1);
+          a2[r][u] = X4[xrow[r] + 2 * j];
+          c2[r][u] = X4[xrow[r] + 2 * j + 1];
+        }
+#pragma unroll
+      for (int r = 0; r < MC; ++r)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) mx[r] = fmaxf(mx[r], block_absmax(a2[r][u], c2[r][u]));
+    }
   }
-  __syncthreads();  // the previous chunk's limbs and maxima are no longer read
+  lds_barrier();  // the previous chunk's limbs and maxima are no longer read
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
     float v = mx[r];
     for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
     if (lane == 0) red[wave * MR + r] = v;
   }
-  __syncthreads();
+  lds_barrier();
   int ex[MC];
 #pragma unroll
   for (int r = 0; r < MC; ++r) {
@@ -489,15 +519,16 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
 
   // the split into the A-fragment layout; blocks of groups past G are zero
   for (int j0 = t; j0 < 4 * G4; j0 += 2 * kMfmaThreads) {
-    float4 a[MC][2], c[MC][2];
+    if constexpr (!kOnePass) {
 #pragma unroll
-    for (int r = 0; r < MC; ++r)
+      for (int r = 0; r < MC; ++r)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const long j = std::min(j0 + u * kMfmaThreads, K8 - 1);
-        a[r][u] = X4[xrow[r] + 2 * j];
-        c[r][u] = X4[xrow[r] + 2 * j + 1];
-      }
+        for (int u = 0; u < 2; ++u) {
+          const long j = std::min(j0 + u * kMfmaThreads, K8 - 1);
+          a[r][u] = X4[xrow[r] + 2 * j];
+          c[r][u] = X4[xrow[r] + 2 * j + 1];
+        }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = j0 + u * kMfmaThreads;
@@ -517,15 +548,18 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   const int rr = lane & 15;
   const int a_off = rr < MC ? (R_ * MR + rr) * 16 : zchunk;
   const int a_g = rr < MC ? 4 * MR * 16 : 0;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (n0 < N)
-    mfma_stream<MC, kSc4, PD>(xa, a_off, a_g, reg, zchunk, wrow, srow, G, S, 0,
-                          (S + PD - 1) / PD * PD, w, s, acc);
+  // the ring's first loads (issued before the staging) are in by now; with
+  // nothing in flight on entry, the waits inside the stream's loop stay exact
+  // (each step waits for its own loads only) instead of draining every ring
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  mfma_stream<MC, kSc4, PD>(xa, a_off, a_g, reg, zchunk, wrow, srow, G, S, 0,
+                            (S + PD - 1) / PD * PD, w, s, acc);
   const int n = n0 + lane;
   if (n0 < N && lane < 16 && n < N) {
 #pragma unroll
@@ -544,7 +578,7 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
 // index passes the item count.
 constexpr int kMfmaMaxExperts = 4096;
 
-template <int MR, bool kSc4>
+template <int MR, bool kSc4, bool kOnePass>
 __global__ void __launch_bounds__(kMfmaThreads)
 grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_index,
              const int32_t *__restrict__ offsets, const uint4 *__restrict__ qw,
@@ -560,8 +594,25 @@ grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_inde
   int *part = pre + E + 1;                                                  // [kMfmaThreads]
   const int n_blocks = (N + kMfmaCols - 1) / kMfmaCols;
 
-  // chunks per expert, then their prefix sum: a serial one over each
-  // thread's run of experts, an inclusive scan of the runs' totals
+  // chunks per expert, then their prefix sum: with E <= 64 one wave's
+  // shuffle scan; otherwise a serial one over each thread's run of experts
+  // and an inclusive scan of the runs' totals
+  if (E <= 64) {
+    if (t < 64) {
+      int cnt = 0;
+      if (t < E) {
+        const int r0 = std::min(std::max(offsets[t], 0), R);
+        const int r1 = std::min(std::max(offsets[t + 1], r0), R);
+        cnt = (r1 - r0 + MR - 1) / MR;
+      }
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(cnt, d);
+        if (t >= d) cnt += v;
+      }
+      if (t < E) pre[t + 1] = cnt;
+      if (t == 0) pre[0] = 0;
+    }
+  } else {
   const int per = (E + kMfmaThreads - 1) / kMfmaThreads;
   const int e_lo = std::min(E, t * per), e_hi = std::min(E, e_lo + per);
   int run = 0;
@@ -581,8 +632,9 @@ grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_inde
   }
   const int base = t > 0 ? part[t - 1] : 0;
   for (int e = e_lo; e < e_hi; ++e) pre[e + 1] += base;
+  if (t == 0) pre[0] = 0;
+  }
   if (t == 0) {
-    pre[0] = 0;
     // the zero chunks (never overwritten; the barrier below orders these
     // stores before any read)
     const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -612,15 +664,15 @@ grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_inde
     const uint4 *wrow = qw + (long(e) * N + nrow) * G;
     const float *srow = sc + (long(e) * N + nrow) * G;
     switch (mc) {
-      case 1: mfma_chunk<MR, 1, kSc4>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow); break;
+      case 1: mfma_chunk<MR, 1, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow); break;
       case 2:
-        if constexpr (MR >= 2) mfma_chunk<MR, 2, kSc4>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 2) mfma_chunk<MR, 2, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
       case 3:
-        if constexpr (MR >= 4) mfma_chunk<MR, 3, kSc4>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 4) mfma_chunk<MR, 3, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
       default:
-        if constexpr (MR >= 4) mfma_chunk<MR, 4, kSc4>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 4) mfma_chunk<MR, 4, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
     }
   }
@@ -660,12 +712,18 @@ hipError_t run_mfma(const MfmaPlan &p, const float *X, const int32_t *token_inde
                     const int32_t *offsets, const int32_t *qw, const float *sc, float *Y, int T,
                     int R, int E, int N, int G, hipStream_t stream) {
   const uint4 *q = reinterpret_cast<const uint4 *>(qw);
-  if (G % 4 == 0)
-    hipLaunchKernelGGL((grouped_mfma<MR, true>), dim3(p.grid), dim3(kMfmaThreads), p.lds, stream,
-                       X, token_index, offsets, q, sc, Y, T, R, E, N, G);
-  else
-    hipLaunchKernelGGL((grouped_mfma<MR, false>), dim3(p.grid), dim3(kMfmaThreads), p.lds, stream,
-                       X, token_index, offsets, q, sc, Y, T, R, E, N, G);
+  const bool one_pass = 4 * ((G + 3) & ~3) <= 2 * kMfmaThreads;
+#define W4A16_GROUPED_MFMA(SC4, ONE)                                                             \
+  hipLaunchKernelGGL((grouped_mfma<MR, SC4, ONE>), dim3(p.grid), dim3(kMfmaThreads), p.lds,      \
+                     stream, X, token_index, offsets, q, sc, Y, T, R, E, N, G)
+  if (G % 4 == 0) {
+    if (one_pass) W4A16_GROUPED_MFMA(true, true);
+    else W4A16_GROUPED_MFMA(true, false);
+  } else {
+    if (one_pass) W4A16_GROUPED_MFMA(false, true);
+    else W4A16_GROUPED_MFMA(false, false);
+  }
+#undef W4A16_GROUPED_MFMA
   return hipGetLastError();
 }
 
