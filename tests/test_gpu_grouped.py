@@ -100,3 +100,25 @@ def test_grouped_guard_band_and_determinism(dev):
     b = run(X, ti, off, q, s, dev)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert oracle.compare_grouped(a, X, ti, off, q, s)["ok"]
+
+
+def test_grouped_many_experts_fallback(dev):
+    # more experts than the matrix-core kernel's work list takes: the
+    # LDS-staged FMA kernel runs instead
+    T, E, topk, N, K = 6, 4100, 3, 20, 96
+    say(f"grouped fallback E={E}")
+    X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=21)
+    q, s = quantize_experts(W)
+    v = oracle.compare_grouped(run(X, ti, off, q, s, dev), X, ti, off, q, s)
+    assert v["ok"], v
+
+
+def test_grouped_long_k_fallback(dev):
+    # K too long to stage even one token row in LDS: the kernel that reads
+    # activations from memory runs instead
+    T, E, topk, N, K = 3, 2, 1, 8, 40960 + 32
+    say(f"grouped fallback K={K}")
+    X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=22)
+    q, s = quantize_experts(W)
+    v = oracle.compare_grouped(run(X, ti, off, q, s, dev), X, ti, off, q, s)
+    assert v["ok"], v
