@@ -50,9 +50,9 @@ PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu"
 SPLIT_PATHS = ("split", "packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
-                "split": ["split.hip"], "packed": ["split.hip"],
+                "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_common.h"],
-                "grouped": ["grouped.hip", "gemv_common.h"]}
+                "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"]}
 
 
 def source_hash(path: str) -> str:
@@ -416,6 +416,13 @@ def main():
         print(json.dumps(line), flush=True)
 
 
+def moe_dtype(wl) -> str:
+    """Arithmetic of the grouped kernel the library picks for this workload."""
+    from int4_weight_only_03_amd import binding
+    k = binding.w4a16_grouped_kernel(wl.T, wl.R, wl.E, wl.N, wl.K)
+    return "f16x2-limb/f32-acc" if k == binding.W4A16_GROUPED_MFMA else "f32"
+
+
 def run_moe(name, args):
     wl = workloads.MOE_WORKLOADS[name]
     print(f"# {name}: T={wl.T} E={wl.E} top-{wl.topk} K={wl.K} N={wl.N} steps={args.steps} "
@@ -424,7 +431,7 @@ def run_moe(name, args):
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": moe_dtype(wl), "data": "synthetic",
         "config": {"workload": name, "T": wl.T, "experts": wl.E, "topk": wl.topk, "K": wl.K,
                    "N": wl.N, "group": 32, "note": wl.note, "parallelism": "none (1 GPU)"},
         "roofline": roof,

@@ -135,17 +135,33 @@ int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scale
  *   scales         float [E][N][K/32]
  *   Y              float [R][N]        Y[r] = X[token_index[r]] . dequant(W_e)^T, e
  *                                      the expert owning slot r
- * All DEVICE memory.  The same arithmetic and tolerance as w4a16_gemm.  An
- * expert with no slot costs one empty workgroup and its weights are not
- * read.  token_index and expert_offsets are read on the device and clamped
- * into range (malformed routing gives wrong values, never an out-of-bounds
- * access).  R == 0 or N == 0 is a no-op; T == 0 with R > 0, E < 1 or
- * E > 65535 is an error; otherwise errors as w4a16_gemm (Y overlapping any
- * input is W4A16_ERR_ARG; token_index and expert_offsets 4-byte aligned).
+ * All DEVICE memory.  The kernel depends on the shape
+ * (w4a16_grouped_kernel): on the matrix cores the arithmetic is that of
+ * w4a16_gemm_split (exact weight codes, two fp16 limbs of each prescaled
+ * activation, fp32 accumulation; a token row holding Inf or NaN gives NaN in
+ * its slots' outputs); otherwise fp32 FMA as w4a16_gemm.  Either way the
+ * tolerance of w4a16_gemm holds.  The weights of an expert with no slot are
+ * not read.  token_index and expert_offsets are read on the device and
+ * clamped into range (malformed routing gives wrong values, never an
+ * out-of-bounds access).  R == 0 or N == 0 is a no-op; T == 0 with R > 0,
+ * E < 1 or E > 65535 is an error; otherwise errors as w4a16_gemm (Y
+ * overlapping any input is W4A16_ERR_ARG; token_index and expert_offsets
+ * 4-byte aligned).
  */
 int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t *expert_offsets,
                        const int32_t *qweight, const float *scales, float *Y, int64_t T,
                        int64_t R, int64_t E, int64_t N, int64_t K, int32_t group, void *stream);
+
+/* Kernels behind w4a16_gemm_grouped. */
+#define W4A16_GROUPED_MFMA 1  /* matrix cores, split-path arithmetic; up to 4096 experts
+                                 and the token rows of a slot chunk staged in LDS */
+#define W4A16_GROUPED_ROWS 2  /* fp32 FMA, token rows staged in LDS */
+#define W4A16_GROUPED_GEMV 3  /* fp32 FMA, activations read from memory */
+
+/* The kernel w4a16_gemm_grouped runs for T tokens, R slots, E experts and an
+ * N x K expert shape (one of W4A16_GROUPED_*), or 0 for a shape it refuses or
+ * treats as a no-op.  Host only; no GPU use. */
+int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
 
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);

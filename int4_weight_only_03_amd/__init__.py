@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     w4a16_abi_version,
     w4a16_gemm,
     w4a16_gemm_grouped,
+    w4a16_grouped_kernel,
     w4a16_gemm_path,
     w4a16_gemm_split,
     w4a16_gemm_swiglu,

@@ -65,6 +65,7 @@ _SIGS = {
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
                                 ctypes.c_int),
+    "w4a16_grouped_kernel": ([ctypes.c_int64] * 5, ctypes.c_int),
     "w4a16_load_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "w4a16_save_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
@@ -194,6 +195,16 @@ def w4a16_gemm_path(X, qweight, scales, Y=None, path: int = W4A16_PATH_AUTO, str
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_path")
     return Y
+
+
+W4A16_GROUPED_MFMA = 1
+W4A16_GROUPED_ROWS = 2
+W4A16_GROUPED_GEMV = 3
+
+
+def w4a16_grouped_kernel(T: int, R: int, E: int, N: int, K: int) -> int:
+    """Kernel of w4a16_gemm_grouped for this shape (W4A16_GROUPED_*), 0 if none."""
+    return load().w4a16_grouped_kernel(T, R, E, N, K)
 
 
 def w4a16_split_workspace_bytes(M: int, N: int, K: int) -> int:

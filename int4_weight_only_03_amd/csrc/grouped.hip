@@ -829,6 +829,15 @@ int compute_units() {
   return cus;
 }
 
+int grouped_kernel(int T, int R, int E, int N, int K) {
+  const int G = K / kGroup;
+  MfmaPlan mp;
+  if (plan_mfma(T, R, E, N, G, 256, mp)) return 1;  // the choice does not depend on the CU count
+  RowsPlan rp;
+  if (plan_rows(R, E, N, G, rp)) return 2;
+  return 3;
+}
+
 hipError_t launch_grouped(const float *X, const int32_t *token_index, const int32_t *offsets,
                           const int32_t *qweight, const float *scales, float *Y, int T, int R,
                           int E, int N, int K, hipStream_t stream) {

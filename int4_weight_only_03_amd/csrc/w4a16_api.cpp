@@ -127,6 +127,13 @@ int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
+  if (T <= 0 || R <= 0 || E <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)
+    return 0;
+  return w4a16::grouped_kernel(int(T), int(R), int(E), int(N), int(K));
+}
+
 size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;

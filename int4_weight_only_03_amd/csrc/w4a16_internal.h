@@ -46,6 +46,9 @@ hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const floa
 
 // Grouped (MoE) GEMM: Y[r] = X[token_index[r]] . dequant(W_e)^T for the
 // expert e whose slot range [offsets[e], offsets[e+1]) holds r.
+// which kernel launch_grouped runs for this shape: 1 matrix cores, 2 fp32
+// FMA with staged token rows, 3 fp32 FMA reading activations from memory
+int grouped_kernel(int T, int R, int E, int N, int K);
 hipError_t launch_grouped(const float *X, const int32_t *token_index, const int32_t *offsets,
                           const int32_t *qweight, const float *scales, float *Y, int T, int R,
                           int E, int N, int K, hipStream_t stream);

@@ -108,6 +108,7 @@ def test_grouped_many_experts_fallback(dev):
     T, E, topk, N, K = 6, 4100, 3, 20, 96
     say(f"grouped fallback E={E}")
     X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=21)
+    assert binding.w4a16_grouped_kernel(T, ti.size, E, N, K) == binding.W4A16_GROUPED_ROWS
     q, s = quantize_experts(W)
     v = oracle.compare_grouped(run(X, ti, off, q, s, dev), X, ti, off, q, s)
     assert v["ok"], v
@@ -119,6 +120,7 @@ def test_grouped_long_k_fallback(dev):
     T, E, topk, N, K = 3, 2, 1, 8, 40960 + 32
     say(f"grouped fallback K={K}")
     X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=22)
+    assert binding.w4a16_grouped_kernel(T, ti.size, E, N, K) == binding.W4A16_GROUPED_GEMV
     q, s = quantize_experts(W)
     v = oracle.compare_grouped(run(X, ti, off, q, s, dev), X, ti, off, q, s)
     assert v["ok"], v

@@ -256,3 +256,16 @@ def test_binding_refuses_host_tensors(lib):
 def test_header_names_match_binding():
     assert set(binding.header_functions()) == set(binding._SIGS)
     assert isinstance(ctypes.sizeof(ctypes.c_void_p), int)
+
+
+def test_grouped_kernel_choice():
+    """w4a16_grouped_kernel: the matrix-core kernel for decode-shaped MoE, the
+    FMA kernels past its limits, 0 for refused shapes (host only)."""
+    from int4_weight_only_03_amd import binding as b
+    assert b.w4a16_grouped_kernel(16, 64, 32, 1024, 7168) == b.W4A16_GROUPED_MFMA
+    assert b.w4a16_grouped_kernel(1, 8, 256, 2048, 7168) == b.W4A16_GROUPED_MFMA
+    assert b.w4a16_grouped_kernel(6, 18, 4100, 20, 96) == b.W4A16_GROUPED_ROWS
+    assert b.w4a16_grouped_kernel(3, 3, 2, 8, 40992) == b.W4A16_GROUPED_GEMV
+    for bad in [(0, 1, 1, 8, 32), (1, 1, 0, 8, 32), (1, 1, 1, 8, 48), (1, 1, 65536, 8, 32),
+                (1, 0, 1, 8, 32)]:
+        assert b.w4a16_grouped_kernel(*bad) == 0
