@@ -52,7 +52,8 @@ SPLIT_PATHS = ("split", "packed")
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_common.h"],
-                "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"]}
+                "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
+                "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"]}
 
 
 def source_hash(path: str) -> str:
@@ -122,18 +123,19 @@ def time_steps(step, steps: int, stream):
     return start.elapsed_time(end) / steps, per_launch_ms, graphed
 
 
-def gpu_leg_moe(name: str, steps: int, warmup: int):
-    """The grouped (MoE) GEMM on a synthetic routed decode batch."""
+def gpu_leg_moe(name: str, steps: int, warmup: int, packed: bool = False):
+    """The grouped (MoE) GEMM on a synthetic routed decode batch; with `packed`
+    the weights are first repacked (w4a16_grouped_pack, timed on its own)."""
     import torch
     import int4_weight_only_03_amd as pkg
 
     wl = workloads.MOE_WORKLOADS[name]
     dev = torch.device("cuda:0")
     X, W, ti, off = workloads.make_moe(name)
-    packed = [pkg.w4a16_quantize(W[e]) for e in range(wl.E)]   # the library's host quantizer
-    qw = np.stack([q for q, _ in packed])
-    sc = np.stack([s for _, s in packed])
-    del packed
+    quantized = [pkg.w4a16_quantize(W[e]) for e in range(wl.E)]   # the library's host quantizer
+    qw = np.stack([q for q, _ in quantized])
+    sc = np.stack([s for _, s in quantized])
+    del quantized
     B = wl.algorithmic_bytes(off)
     copies = max(1, -(-2 * MALL_BYTES // B))
     Xd, Qd, Sd = (torch.from_numpy(a).to(dev) for a in (X, qw, sc))
@@ -142,10 +144,24 @@ def gpu_leg_moe(name: str, steps: int, warmup: int):
              torch.empty((wl.R, wl.N), dtype=torch.float32, device=dev)) for _ in range(copies)]
     del Xd, Qd, Sd
     stream = torch.cuda.current_stream(dev)
+    repack_ms = None
+    if packed:  # one-time repack of every copy; its time is reported, not in the steps
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bufs = []
+        a.record(stream)
+        for x, q, s, y in sets:
+            bufs.append(pkg.w4a16_grouped_pack(q, s))
+        b.record(stream)
+        torch.cuda.synchronize()
+        repack_ms = a.elapsed_time(b) / len(sets)
+        sets = [(x, pb, None, y) for (x, q, s, y), pb in zip(sets, bufs)]
 
     def step(i):
         x, q, s, y = sets[i % copies]
-        pkg.w4a16_gemm_grouped(x, Id, Od, q, s, y)
+        if packed:
+            pkg.w4a16_gemm_grouped_packed(x, Id, Od, q, wl.E, wl.N, y)
+        else:
+            pkg.w4a16_gemm_grouped(x, Id, Od, q, s, y)
 
     for i in range(warmup):
         step(i)
@@ -153,15 +169,18 @@ def gpu_leg_moe(name: str, steps: int, warmup: int):
     ms_per_step, per_launch_ms, graphed = time_steps(step, steps, stream)
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
+    path = "grouped-packed" if packed else "grouped"
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name, "grouped")}
+            "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name, path)}
     med = statistics.median(per_launch_ms)
     active = int(np.count_nonzero(np.diff(off)))
     extra = {"graph_replay": graphed, "rotation_copies": copies, "algorithmic_bytes": B,
              "flops": wl.flops(), "per_launch_event_us_median": med * 1e3,
-             "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9, "path": "grouped",
+             "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9, "path": path,
              "active_experts": active, "hbm_frac": gbs / HBM_PEAK_GBS,
              "fp32_frac": tfs / FP32_PEAK_TFLOPS}
+    if repack_ms is not None:
+        extra["repack_ms_one_time"] = repack_ms
     y0 = sets[0][3].cpu().numpy()
     return gbs, "GB/s", ms_per_step, roof, extra, (X, qw, sc, ti, off, y0)
 
@@ -371,7 +390,8 @@ def main():
                         workloads.ORDER + list(workloads.MOE_WORKLOADS)))
     ap.add_argument("--path", default="auto",
                     help="kernel path(s), comma-separated: auto, gemv, tile, split, packed, "
-                         "swiglu (grouped-MoE workloads always run the grouped kernel)")
+                         "swiglu; grouped-MoE workloads run the grouped kernel on the "
+                         "public layout, or with 'packed' on the repacked weights")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -391,7 +411,11 @@ def main():
             ap.error(f"unknown path {p!r}")
     for name in names:
         if name in workloads.MOE_WORKLOADS:
-            run_moe(name, args)
+            # "packed": the repacked grouped weights; any other path: the public layout
+            if any(p != "packed" for p in paths):
+                run_moe(name, args)
+            if "packed" in paths:
+                run_moe(name, args, packed=True)
     names = [n for n in names if n not in workloads.MOE_WORKLOADS]
     for name, path in [(n, p) for n in names for p in paths]:
         wl = workloads.WORKLOADS[name]
@@ -423,11 +447,11 @@ def moe_dtype(wl) -> str:
     return "f16x2-limb/f32-acc" if k == binding.W4A16_GROUPED_MFMA else "f32"
 
 
-def run_moe(name, args):
+def run_moe(name, args, packed=False):
     wl = workloads.MOE_WORKLOADS[name]
     print(f"# {name}: T={wl.T} E={wl.E} top-{wl.topk} K={wl.K} N={wl.N} steps={args.steps} "
-          f"path=grouped", file=sys.stderr, flush=True)
-    value, unit, ms, roof, extra, out = gpu_leg_moe(name, args.steps, args.warmup)
+          f"path={'grouped-packed' if packed else 'grouped'}", file=sys.stderr, flush=True)
+    value, unit, ms, roof, extra, out = gpu_leg_moe(name, args.steps, args.warmup, packed)
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

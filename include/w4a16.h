@@ -152,6 +152,50 @@ int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t
                        const int32_t *qweight, const float *scales, float *Y, int64_t T,
                        int64_t R, int64_t E, int64_t N, int64_t K, int32_t group, void *stream);
 
+/*
+ * Bytes of the packed expert weights w4a16_grouped_pack writes for E experts
+ * of N x K (0 if the shape is invalid): E * ceil(N/16) * ceil(K/128) * 1280,
+ * the size of qweight plus scales up to the padding of N to 16 rows and of
+ * the group count to a multiple of 4.
+ */
+size_t w4a16_grouped_pack_bytes(int64_t E, int64_t N, int64_t K);
+
+/*
+ * One-time repack of expert weights qweight[E][N][K/8] and scales[E][N][K/32]
+ * (DEVICE memory, the layouts of w4a16_gemm_grouped) into the grouped matrix-
+ * core kernel's private layout, `packed` (DEVICE memory owned by the caller,
+ * 16-byte aligned, at least w4a16_grouped_pack_bytes(E, N, K) bytes,
+ * overlapping no input): the optional repack into a kernel-private layout
+ * that the pages allow for the weights; bits are moved only.  Layout, for
+ * expert e, 16-row tile t (T16 = ceil(N/16) tiles) and 4-group step s
+ * (S4 = ceil(K/128) steps), block b = (e*T16 + t)*S4 + s:
+ *   bytes [0, E*T16*S4*1024): at b*64 + l chunks of 16 bytes, l = c + 16 R:
+ *     word R of groups 4s, 4s+1, 4s+2, 4s+3 of row 16t + c;
+ *   then E*T16*S4*256 bytes: at float (b*16 + c)*4 + q, the scale of group
+ *     4s + q of row 16t + c.
+ * Rows past N and groups past K/32 hold the word 0x88888888 (every code 8,
+ * weight 0) and scale 0.  Every weight load of the packed GEMM then reads
+ * whole contiguous kilobytes.  Enqueued on `stream`.  N == 0 is a no-op;
+ * errors as w4a16_gemm_grouped (W4A16_ERR_ARG for a NULL, misaligned, too
+ * small or overlapping `packed`).
+ */
+int w4a16_grouped_pack(const int32_t *qweight, const float *scales, int64_t E, int64_t N,
+                       int64_t K, int32_t group, void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * w4a16_gemm_grouped on weights packed by w4a16_grouped_pack(..., E, N, K,
+ * ...): the same result, bit for bit, as w4a16_gemm_grouped on the unpacked
+ * weights when that runs the matrix-core kernel (W4A16_GROUPED_MFMA), which
+ * is the only kernel with a packed form: shapes for which
+ * w4a16_grouped_kernel is not W4A16_GROUPED_MFMA return W4A16_ERR_SHAPE.
+ * Otherwise errors as w4a16_gemm_grouped (`packed` 16-byte aligned, Y
+ * overlapping it is W4A16_ERR_ARG).
+ */
+int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
+                              const int32_t *expert_offsets, const void *packed, float *Y,
+                              int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
+                              int32_t group, void *stream);
+
 /* Kernels behind w4a16_gemm_grouped. */
 #define W4A16_GROUPED_MFMA 1  /* matrix cores, split-path arithmetic; up to 4096 experts
                                  and the token rows of a slot chunk staged in LDS */

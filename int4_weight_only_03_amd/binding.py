@@ -66,6 +66,12 @@ _SIGS = {
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
                                 ctypes.c_int),
     "w4a16_grouped_kernel": ([ctypes.c_int64] * 5, ctypes.c_int),
+    "w4a16_grouped_pack_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
+    "w4a16_grouped_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                            ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                            ctypes.c_void_p], ctypes.c_int),
+    "w4a16_gemm_grouped_packed": ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
+                                  [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_load_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "w4a16_save_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
@@ -205,6 +211,66 @@ W4A16_GROUPED_GEMV = 3
 def w4a16_grouped_kernel(T: int, R: int, E: int, N: int, K: int) -> int:
     """Kernel of w4a16_gemm_grouped for this shape (W4A16_GROUPED_*), 0 if none."""
     return load().w4a16_grouped_kernel(T, R, E, N, K)
+
+
+def w4a16_grouped_pack_bytes(E: int, N: int, K: int) -> int:
+    return int(load().w4a16_grouped_pack_bytes(E, N, K))
+
+
+def w4a16_grouped_pack(qweight, scales, packed=None, stream=None):
+    """Repack device expert weights qweight [E][N][K/8] and scales [E][N][K/32]
+    for w4a16_gemm_grouped_packed (uint8 tensor)."""
+    import torch
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    if qweight.dim() != 3 or scales.dim() != 3:
+        raise ValueError("qweight and scales must be 3-D [E][N][...]")
+    E, N, K8 = qweight.shape
+    K = 8 * K8
+    if tuple(scales.shape) != (E, N, K // GROUP):
+        raise ValueError(f"shapes disagree: qweight {tuple(qweight.shape)}, "
+                         f"scales {tuple(scales.shape)}")
+    need = w4a16_grouped_pack_bytes(E, N, K) if N else 0
+    if packed is None:
+        packed = torch.empty(max(need, 1), dtype=torch.uint8, device=qweight.device)
+    packed = _dev(packed, torch.uint8, "packed")
+    st = load().w4a16_grouped_pack(qweight.data_ptr(), scales.data_ptr(), E, N, K, GROUP,
+                                   packed.data_ptr(), packed.numel(),
+                                   _stream_ptr(stream, qweight.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_grouped_pack")
+    return packed
+
+
+def w4a16_gemm_grouped_packed(X, token_index, expert_offsets, packed, E: int, N: int, Y=None,
+                              stream=None):
+    """Grouped MoE GEMM on weights from w4a16_grouped_pack (E experts of N rows)."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    token_index = _dev(token_index, torch.int32, "token_index")
+    expert_offsets = _dev(expert_offsets, torch.int32, "expert_offsets")
+    packed = _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    T, K = X.shape
+    R = token_index.numel()
+    if expert_offsets.numel() != E + 1:
+        raise ValueError("expert_offsets must have E + 1 entries")
+    if packed.numel() < w4a16_grouped_pack_bytes(E, N, K):
+        raise ValueError("packed buffer smaller than w4a16_grouped_pack_bytes(E, N, K)")
+    if Y is None:
+        Y = torch.empty((R, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (R, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(R, N)}")
+    st = load().w4a16_gemm_grouped_packed(X.data_ptr(), token_index.data_ptr(),
+                                          expert_offsets.data_ptr(), packed.data_ptr(),
+                                          Y.data_ptr(), T, R, E, N, K, GROUP,
+                                          _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_grouped_packed")
+    return Y
 
 
 def w4a16_split_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -258,7 +258,7 @@ grouped_rows(const float *__restrict__ X, const int32_t *__restrict__ token_inde
 
 // ------------------------------------------------------------ matrix cores
 //
-// grouped_mfma<MR, kSc4>: the same product on v_mfma_f32_16x16x32_f16, with
+// grouped_mfma<MR, kSrc, kOnePass>: the same product on v_mfma_f32_16x16x32_f16, with
 // the split path's arithmetic: exact weight codes q - 8, two fp16 limbs of
 // each prescaled activation, fp32 accumulation, one fp32 FMA per group for
 // the scale, the row's power of two undone at the store.  Rows 0..MR-1 of the
@@ -266,41 +266,46 @@ grouped_rows(const float *__restrict__ X, const int32_t *__restrict__ token_inde
 // zero, so each weight is converted once and met by all the slots in one
 // instruction instead of one FMA per slot.
 //
-// A workgroup of kMfmaWaves waves serves one expert, kMfmaCols consecutive
-// output columns (16 per wave) and one chunk of MR of the expert's slots
-// (chunks c0, c0 + C, ... of that expert):
-//  * the chunk's token rows are read once for each row's maximum (its
-//    power-of-two exponent), then K is taken in windows of W groups: the
-//    window's limbs are split into LDS as MFMA A fragments (16-byte chunk
-//    ((g - w0)*4 + b)*MR + r holds the 8 limbs of k block b of group g of
-//    slot r; hi region, then lo region, each ending with a zero chunk that the
-//    tile rows past the chunk's slots read) and the waves stream that window.
-//    Windows keep the workgroup's LDS under 64 KB: larger allocations left
-//    many compute units unable to take a workgroup.
+// A workgroup of kMfmaWaves waves takes work items: (expert, chunk of up to
+// MR of the expert's slots, block of kMfmaCols = 16 x kMfmaWaves columns).
+//  * staging: the chunk's token rows are read (once, before the weight loads,
+//    when they fit in registers) for each row's maximum, i.e. its
+//    power-of-two exponent, and split into LDS as MFMA A fragments: 16-byte
+//    chunk (g*4 + b)*MR + r holds the 8 limbs of k block b of group g of slot
+//    r; hi region, then lo region, each followed by a zero region of 4 groups
+//    that steps past the last group read.  Tile rows past the chunk's slots
+//    read slot rows too: they only make output rows that are never stored.
 //  * each wave streams its 16 weight rows.  Lane (c, R), R the lane's 16-lane
 //    row, loads the 16 bytes of group 4s + R of weight row c, so one load
 //    covers 4 groups of 16 rows with 64 contiguous bytes per row.  Two rounds
 //    of lane swaps across the four 16-lane rows transpose that to word R of
 //    each of the 4 groups in lane (c, R): the MFMA's B operand.  Per group:
 //    hi and lo MFMAs into one zeroed tile, then one FMA per slot row with the
-//    group's scale.  Loads run kMfmaPD steps ahead, across windows.
-//  * the barriers between phases wait for LDS traffic only, never for the
-//    weight loads in flight.
+//    group's scale.  Loads run kMfmaPD steps ahead.
+//  * the staging barriers wait for LDS traffic only, never for the weight
+//    loads in flight.
 //  * slot rows 0..MR-1 of the result tile sit in lanes 0..15 (column c, 4
 //    rows each), which write Y.
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kMfmaCols = 16 * kMfmaWaves;
 constexpr int kMfmaPD = 8;                 // 4-group steps in flight per wave
-// the ring depth: shallower when the scales take four loads (G % 4 != 0), to
-// stay within the registers of 8 waves per compute unit
-template <bool kSc4>
-constexpr int kMfmaDepth = kSc4 ? kMfmaPD : kMfmaPD - 2;
+// Where a wave's weights and scales come from: the public layout with one
+// 16-byte scale load per step (G % 4 == 0), the public layout with four
+// scale loads (G % 4 != 0), or the packed layout of w4a16_grouped_pack.
+constexpr int kSrcPublic = 0;
+constexpr int kSrcPublicScalar = 1;
+constexpr int kSrcPacked = 2;
+
+// the ring depth: shallower when the scales take four loads, to stay within
+// the registers of 8 waves per compute unit
+template <int kSrc>
+constexpr int kMfmaDepth = kSrc == kSrcPublicScalar ? kMfmaPD - 2 : kMfmaPD;
 constexpr int kMfmaMaxLds = 150 * 1024;
 
-// bytes of one limb region for MR rows and a window of W groups (with its
-// zero chunk), and of the whole LDS image
-__host__ __device__ constexpr int mfma_region_bytes(int MR, int G4) { return G4 * 4 * MR * 16 + 16; }
+// bytes of one limb region for MR rows and G4 groups (with its zero region of
+// 4 groups), and of the whole LDS image (without the work list)
+__host__ __device__ constexpr int mfma_region_bytes(int MR, int G4) { return (G4 + 4) * 4 * MR * 16; }
 
 __host__ __device__ constexpr int mfma_lds_bytes(int MR, int G4) {
   return 2 * mfma_region_bytes(MR, G4) + kMfmaWaves * MR * 4;
@@ -321,14 +326,27 @@ __device__ __forceinline__ float block_absmax(float4 a, float4 c) {
                fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
 }
 
-// one 4-group step of weights (lane (c, R): group 4*step + R of its row) and
-// the 4 scales of its row
-template <bool kSc4>
-__device__ __forceinline__ void mfma_load(const uint4 *__restrict__ wrow,
-                                          const float *__restrict__ srow, int G, int step, int R,
-                                          uint4 &w, float4 &s) {
-  w = load_stream16(wrow + std::min(4 * step + R, G - 1));
-  if constexpr (kSc4) {
+// one 4-group step of weights and the 4 scales of the lane's row.  Public
+// layout: lane (c, R) loads group 4*step + R of its row (wrow, srow: the
+// row); packed layout: the lane's 16 bytes of the tile's step block, already
+// word R of each of the 4 groups (wrow: the tile's first block plus the lane;
+// srow: the tile's first scale block plus 4 c)
+template <int kSrc>
+__device__ __forceinline__ void mfma_load_w(const uint4 *__restrict__ wrow, int G, int step, int R,
+                                            uint4 &w) {
+  if constexpr (kSrc == kSrcPacked) {
+    w = load_stream16(wrow + long(step) * 64);
+  } else {
+    w = load_stream16(wrow + std::min(4 * step + R, G - 1));
+  }
+}
+
+template <int kSrc>
+__device__ __forceinline__ void mfma_load_s(const float *__restrict__ srow, int G, int step,
+                                            float4 &s) {
+  if constexpr (kSrc == kSrcPacked) {
+    s = *reinterpret_cast<const float4 *>(srow + long(step) * 64);
+  } else if constexpr (kSrc == kSrcPublic) {
     s = *reinterpret_cast<const float4 *>(srow + 4 * step);
   } else {
     s.x = srow[std::min(4 * step + 0, G - 1)];
@@ -336,6 +354,14 @@ __device__ __forceinline__ void mfma_load(const uint4 *__restrict__ wrow,
     s.z = srow[std::min(4 * step + 2, G - 1)];
     s.w = srow[std::min(4 * step + 3, G - 1)];
   }
+}
+
+template <int kSrc>
+__device__ __forceinline__ void mfma_load(const uint4 *__restrict__ wrow,
+                                          const float *__restrict__ srow, int G, int step, int R,
+                                          uint4 &w, float4 &s) {
+  mfma_load_w<kSrc>(wrow, G, step, R, w);
+  mfma_load_s<kSrc>(srow, G, step, s);
 }
 
 // lane row R holds words 0..3 of group R; afterwards word R of groups 0..3
@@ -354,81 +380,82 @@ __device__ __forceinline__ void transpose4(uint32_t &v0, uint32_t &v1, uint32_t 
   v3 = d[1];
 }
 
-// steps [s_begin, s_end) of the wave's 16 columns for MC slot rows, s_begin a
-// multiple of kMfmaPD.  w/s form a ring of kMfmaPD 4-group steps holding
-// steps s_begin.. on entry; each step reloads its slot kMfmaPD steps ahead:
-// the weights once they are converted, the scales once the FMAs have used
-// them.  Each reload follows the last use of the slot's old value and is
-// pinned there, so the ring keeps its registers across the loop's back edge
-// and a step waits only for its own loads (a reload moved later, or a copy of
-// a value still in flight, would make a step wait for all loads).  Steps at
-// or past S read the zero chunk and add exactly 0, so the ring's steps run
-// without branches.  LDS group offsets are relative to the window's first
-// group, 4 * s_begin.
-template <int MC, bool kSc4, int PD>
-__device__ __forceinline__ void mfma_stream(const unsigned char *__restrict__ xa, int a_off,
-                                            int a_g, int reg, int zchunk,
-                                            const uint4 *__restrict__ wrow,
-                                            const float *__restrict__ srow, int G, int S,
-                                            int s_begin, int s_end, uint4 (&w)[PD],
-                                            float4 (&s)[PD], float (&acc)[4]) {
-  const int R = (threadIdx.x & 63) >> 4;
+// one 4-group step: operand reads, weight conversion, reload of the ring
+// slot kMfmaPD steps ahead (pinned right after the slot's last use of the
+// weights; the scales after the FMAs), MFMAs and scale FMAs.  kLive: the step
+// is below S and its reload in range (no clamps, no selects); otherwise a
+// step at or past S reads the zero chunk and adds exactly 0, and the reload
+// is clamped to the last step.
+template <int MR, int MC, int kSrc>
+__device__ __forceinline__ void mfma_step(const unsigned char *__restrict__ xa, int a_off,
+                                          int reg, int zregion, const uint4 *__restrict__ wrow,
+                                          const float *__restrict__ srow, int G, int S, int step,
+                                          int R, uint4 &w, float4 &s, float (&acc)[4]) {
+  constexpr int AG = 4 * MR * 16;  // bytes between consecutive groups' A fragments
+  constexpr int PD = kMfmaDepth<kSrc>;
   const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s0 = s_begin; s0 < s_end; s0 += PD) {
+  const int next = std::min(step + PD, S - 1);
+  // a step at or past S reads the zero region (4 groups of zero fragments,
+  // same stride) and adds exactly 0
+  const unsigned char *ap = xa + (step < S ? a_off + 4 * step * AG : zregion);
+  half8_t ah[4], al[4];
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const int step = s0 + p;
-      const int next = std::min(step + PD, S - 1);
-      const bool live = step < S;
-      // operand reads for the 4 groups, then the weight conversions
-      const int ag = live ? a_g : 0;
-      const unsigned char *ap = xa + (live ? a_off + 4 * (step - s_begin) * a_g : zchunk);
-      half8_t ah[4], al[4];
+  for (int q = 0; q < 4; ++q) {
+    ah[q] = *reinterpret_cast<const half8_t *>(ap + q * AG);
+    al[q] = *reinterpret_cast<const half8_t *>(ap + q * AG + reg);
+  }
+  uint32_t v0 = w.x, v1 = w.y, v2 = w.z, v3 = w.w;
+  if constexpr (kSrc != kSrcPacked) transpose4(v0, v1, v2, v3);
+  const half8_t b0 = nibbles_to_f16(v0), b1 = nibbles_to_f16(v1);
+  const half8_t b2 = nibbles_to_f16(v2), b3 = nibbles_to_f16(v3);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_load_w<kSrc>(wrow, G, next, R, w);
+  __builtin_amdgcn_sched_barrier(0);
+  // the 4 groups are independent: hi MFMAs, lo MFMAs, then the scales
+  floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[0], b0, zero, 0, 0, 0);
+  floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[1], b1, zero, 0, 0, 0);
+  floatx4 d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[2], b2, zero, 0, 0, 0);
+  floatx4 d3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[3], b3, zero, 0, 0, 0);
+  d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[0], b0, d0, 0, 0, 0);
+  d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[1], b1, d1, 0, 0, 0);
+  d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[2], b2, d2, 0, 0, 0);
+  d3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[3], b3, d3, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ah[q] = *reinterpret_cast<const half8_t *>(ap + q * ag);
-        al[q] = *reinterpret_cast<const half8_t *>(ap + q * ag + reg);
-      }
-      uint32_t v0 = w[p].x, v1 = w[p].y, v2 = w[p].z, v3 = w[p].w;
-      transpose4(v0, v1, v2, v3);
-      const half8_t b0 = nibbles_to_f16(v0), b1 = nibbles_to_f16(v1);
-      const half8_t b2 = nibbles_to_f16(v2), b3 = nibbles_to_f16(v3);
-      __builtin_amdgcn_sched_barrier(0);
-      w[p] = load_stream16(wrow + std::min(4 * next + R, G - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      // the 4 groups are independent: hi MFMAs, lo MFMAs, then the scales
-      floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[0], b0, zero, 0, 0, 0);
-      floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[1], b1, zero, 0, 0, 0);
-      floatx4 d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[2], b2, zero, 0, 0, 0);
-      floatx4 d3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[3], b3, zero, 0, 0, 0);
-      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[0], b0, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[1], b1, d1, 0, 0, 0);
-      d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[2], b2, d2, 0, 0, 0);
-      d3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[3], b3, d3, 0, 0, 0);
+  for (int i = 0; i < MC; ++i) {
+    acc[i] = fmaf(s.x, d0[i], acc[i]);
+    acc[i] = fmaf(s.y, d1[i], acc[i]);
+    acc[i] = fmaf(s.z, d2[i], acc[i]);
+    acc[i] = fmaf(s.w, d3[i], acc[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_load_s<kSrc>(srow, G, next, s);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// the wave's 16 columns over all S steps for MC slot rows.  w/s form a ring
+// of PD 4-group steps holding steps 0..PD-1 on entry; each step reloads its
+// slot PD steps ahead, right after the slot's last use, so the ring keeps its
+// registers across the loop's back edge and a step waits only for its own
+// loads (a reload moved later, or a copy of a value still in flight, would
+// make a step wait for all loads).  The loop runs whole rings, the steps past
+// S adding 0, so it has no branch inside.
+template <int MR, int MC, int kSrc, int PD>
+__device__ __forceinline__ void mfma_stream(const unsigned char *__restrict__ xa, int a_off,
+                                            int reg, int zregion, const uint4 *__restrict__ wrow,
+                                            const float *__restrict__ srow, int G, int S,
+                                            uint4 (&w)[PD], float4 (&s)[PD], float (&acc)[4]) {
+  static_assert(PD == kMfmaDepth<kSrc>, "ring depth");
+  const int R = (threadIdx.x & 63) >> 4;
+  for (int s0 = 0; s0 < S; s0 += PD) {
 #pragma unroll
-      for (int i = 0; i < MC; ++i) {
-        acc[i] = fmaf(s[p].x, d0[i], acc[i]);
-        acc[i] = fmaf(s[p].y, d1[i], acc[i]);
-        acc[i] = fmaf(s[p].z, d2[i], acc[i]);
-        acc[i] = fmaf(s[p].w, d3[i], acc[i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kSc4) {
-        s[p] = *reinterpret_cast<const float4 *>(srow + 4 * next);
-      } else {
-        s[p].x = srow[std::min(4 * next + 0, G - 1)];
-        s[p].y = srow[std::min(4 * next + 1, G - 1)];
-        s[p].z = srow[std::min(4 * next + 2, G - 1)];
-        s[p].w = srow[std::min(4 * next + 3, G - 1)];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int p = 0; p < PD; ++p)
+      mfma_step<MR, MC, kSrc>(xa, a_off, reg, zregion, wrow, srow, G, S, s0 + p, R, w[p], s[p],
+                              acc);
   }
 }
 
-// one chunk of MC (<= MR) slots: row maxima, then per window of W groups the
-// limb split and the stream.  Rows past MC of the tile read the zero chunk.
-template <int MR, int MC, bool kSc4, bool kOnePass>
+// one chunk of MC (<= MR) slots: row maxima, the limb split, the stream.
+template <int MR, int MC, int kSrc, bool kOnePass>
 __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
                                            const int32_t *__restrict__ token_index,
                                            unsigned char *__restrict__ xa, float *__restrict__ red,
@@ -441,11 +468,11 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
   const int K8 = G * 4;
   const int S = G4 / 4;
   const int reg = mfma_region_bytes(MR, G4);
-  const int zchunk = G4 * 4 * MR * 16;
+  const int zregion = G4 * 4 * MR * 16;
   const float4 *X4 = reinterpret_cast<const float4 *>(X);
   const long K4 = long(K8) * 2;
   const int R_ = lane >> 4;
-  constexpr int PD = kMfmaDepth<kSc4>;
+  constexpr int PD = kMfmaDepth<kSrc>;
 
   long xrow[MC];  // float4 offset of each slot's token row
 #pragma unroll
@@ -471,7 +498,7 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
   uint4 w[PD];
   float4 s[PD];
 #pragma unroll
-  for (int p = 0; p < PD; ++p) mfma_load<kSc4>(wrow, srow, G, std::min(p, S - 1), R_, w[p], s[p]);
+  for (int p = 0; p < PD; ++p) mfma_load<kSrc>(wrow, srow, G, std::min(p, S - 1), R_, w[p], s[p]);
 
   // row maxima
   float mx[MC];
@@ -550,16 +577,15 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
   }
   lds_barrier();
 
-  const int rr = lane & 15;
-  const int a_off = rr < MC ? (R_ * MR + rr) * 16 : zchunk;
-  const int a_g = rr < MC ? 4 * MR * 16 : 0;
+  // tile rows past MC read slot rows of the chunk as well: they only make
+  // output rows that are never stored, and every lane keeps one stride
+  const int a_off = (R_ * MR + std::min(lane & 15, MC - 1)) * 16;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   // the ring's first loads (issued before the staging) are in by now; with
   // nothing in flight on entry, the waits inside the stream's loop stay exact
   // (each step waits for its own loads only) instead of draining every ring
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  mfma_stream<MC, kSc4, PD>(xa, a_off, a_g, reg, zchunk, wrow, srow, G, S, 0,
-                            (S + PD - 1) / PD * PD, w, s, acc);
+  mfma_stream<MR, MC, kSrc, PD>(xa, a_off, reg, zregion, wrow, srow, G, S, w, s, acc);
   const int n = n0 + lane;
   if (n0 < N && lane < 16 && n < N) {
 #pragma unroll
@@ -578,7 +604,7 @@ __device__ __forceinline__ void mfma_chunk(const float *__restrict__ X,
 // index passes the item count.
 constexpr int kMfmaMaxExperts = 4096;
 
-template <int MR, bool kSc4, bool kOnePass>
+template <int MR, int kSrc, bool kOnePass>
 __global__ void __launch_bounds__(kMfmaThreads)
 grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_index,
              const int32_t *__restrict__ offsets, const uint4 *__restrict__ qw,
@@ -634,12 +660,12 @@ grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_inde
   for (int e = e_lo; e < e_hi; ++e) pre[e + 1] += base;
   if (t == 0) pre[0] = 0;
   }
-  if (t == 0) {
-    // the zero chunks (never overwritten; the barrier below orders these
-    // stores before any read)
+  // the zero regions after each limb region (never overwritten; the barrier
+  // below orders these stores before any read)
+  for (int i = t; i < 4 * 4 * MR; i += kMfmaThreads) {
     const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    *reinterpret_cast<float4 *>(xa + G4 * 4 * MR * 16) = z4;
-    *reinterpret_cast<float4 *>(xa + reg + G4 * 4 * MR * 16) = z4;
+    *reinterpret_cast<float4 *>(xa + G4 * 4 * MR * 16 + i * 16) = z4;
+    *reinterpret_cast<float4 *>(xa + reg + G4 * 4 * MR * 16 + i * 16) = z4;
   }
   __syncthreads();
 
@@ -660,19 +686,30 @@ grouped_mfma(const float *__restrict__ X, const int32_t *__restrict__ token_inde
     const int mc = std::min(MR, r1 - r0 - m0);
     const int rbase = r0 + m0;
     const int n0 = cb * kMfmaCols + (t >> 6) * 16;
-    const long nrow = std::min(n0 + (lane & 15), N - 1);
-    const uint4 *wrow = qw + (long(e) * N + nrow) * G;
-    const float *srow = sc + (long(e) * N + nrow) * G;
+    const uint4 *wrow;
+    const float *srow;
+    if constexpr (kSrc == kSrcPacked) {
+      // the wave's 16-row tile (clamped: waves past N compute but store nothing)
+      const long tiles = (N + 15) / 16;
+      const long tile = long(e) * tiles + std::min(long(n0 / 16), tiles - 1);
+      const long S4 = (G + 3) / 4;
+      wrow = qw + tile * S4 * 64 + lane;
+      srow = sc + (tile * S4 * 16 + (lane & 15)) * 4;
+    } else {
+      const long nrow = std::min(n0 + (lane & 15), N - 1);
+      wrow = qw + (long(e) * N + nrow) * G;
+      srow = sc + (long(e) * N + nrow) * G;
+    }
     switch (mc) {
-      case 1: mfma_chunk<MR, 1, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow); break;
+      case 1: mfma_chunk<MR, 1, kSrc, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow); break;
       case 2:
-        if constexpr (MR >= 2) mfma_chunk<MR, 2, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 2) mfma_chunk<MR, 2, kSrc, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
       case 3:
-        if constexpr (MR >= 4) mfma_chunk<MR, 3, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 4) mfma_chunk<MR, 3, kSrc, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
       default:
-        if constexpr (MR >= 4) mfma_chunk<MR, 4, kSc4, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
+        if constexpr (MR >= 4) mfma_chunk<MR, 4, kSrc, kOnePass>(X, token_index, xa, red, Y, T, N, G, rbase, n0, wrow, srow);
         break;
     }
   }
@@ -709,22 +746,84 @@ bool plan_mfma(int T, int R, int E, int N, int G, int cus, MfmaPlan &p) {
 
 template <int MR>
 hipError_t run_mfma(const MfmaPlan &p, const float *X, const int32_t *token_index,
-                    const int32_t *offsets, const int32_t *qw, const float *sc, float *Y, int T,
-                    int R, int E, int N, int G, hipStream_t stream) {
-  const uint4 *q = reinterpret_cast<const uint4 *>(qw);
+                    const int32_t *offsets, const uint4 *qw, const float *sc, bool packed,
+                    float *Y, int T, int R, int E, int N, int G, hipStream_t stream) {
   const bool one_pass = 4 * ((G + 3) & ~3) <= 2 * kMfmaThreads;
-#define W4A16_GROUPED_MFMA(SC4, ONE)                                                             \
-  hipLaunchKernelGGL((grouped_mfma<MR, SC4, ONE>), dim3(p.grid), dim3(kMfmaThreads), p.lds,      \
-                     stream, X, token_index, offsets, q, sc, Y, T, R, E, N, G)
-  if (G % 4 == 0) {
-    if (one_pass) W4A16_GROUPED_MFMA(true, true);
-    else W4A16_GROUPED_MFMA(true, false);
-  } else {
-    if (one_pass) W4A16_GROUPED_MFMA(false, true);
-    else W4A16_GROUPED_MFMA(false, false);
+  const int src = packed ? kSrcPacked : (G % 4 == 0 ? kSrcPublic : kSrcPublicScalar);
+#define W4A16_GROUPED_MFMA(SRC, ONE)                                                             \
+  hipLaunchKernelGGL((grouped_mfma<MR, SRC, ONE>), dim3(p.grid), dim3(kMfmaThreads), p.lds,      \
+                     stream, X, token_index, offsets, qw, sc, Y, T, R, E, N, G)
+  switch (src * 2 + (one_pass ? 1 : 0)) {
+    case kSrcPublic * 2 + 1: W4A16_GROUPED_MFMA(kSrcPublic, true); break;
+    case kSrcPublic * 2: W4A16_GROUPED_MFMA(kSrcPublic, false); break;
+    case kSrcPublicScalar * 2 + 1: W4A16_GROUPED_MFMA(kSrcPublicScalar, true); break;
+    case kSrcPublicScalar * 2: W4A16_GROUPED_MFMA(kSrcPublicScalar, false); break;
+    case kSrcPacked * 2 + 1: W4A16_GROUPED_MFMA(kSrcPacked, true); break;
+    default: W4A16_GROUPED_MFMA(kSrcPacked, false); break;
   }
 #undef W4A16_GROUPED_MFMA
   return hipGetLastError();
+}
+
+hipError_t run_mfma_any(const MfmaPlan &p, const float *X, const int32_t *token_index,
+                        const int32_t *offsets, const uint4 *qw, const float *sc, bool packed,
+                        float *Y, int T, int R, int E, int N, int G, hipStream_t stream) {
+  switch (p.MR) {
+    case 1: return run_mfma<1>(p, X, token_index, offsets, qw, sc, packed, Y, T, R, E, N, G, stream);
+    case 2: return run_mfma<2>(p, X, token_index, offsets, qw, sc, packed, Y, T, R, E, N, G, stream);
+    default: return run_mfma<4>(p, X, token_index, offsets, qw, sc, packed, Y, T, R, E, N, G, stream);
+  }
+}
+
+// ------------------------------------------------------------ repack
+//
+// The packed layout of w4a16_grouped_pack: for expert e, 16-row tile t
+// (T16 = ceil(N/16) tiles) and 4-group step s (S4 = ceil(G/4) steps), block
+// b = (e*T16 + t)*S4 + s holds
+//  * 64 chunks of 16 bytes at b*64 + l: for lane l = c + 16 R, word R of
+//    groups 4s, 4s+1, 4s+2, 4s+3 of row 16t + c (the MFMA B operand after
+//    the lane transpose of the public layout);
+//  * after all weight blocks, 16 x 4 scales at float (b*16 + c)*4 + q: the
+//    scale of group 4s + q of row 16t + c.
+// Rows past N and groups past G hold the word 0x88888888 (every code 8, so
+// weight 0) and scale 0.  One thread per 16-byte chunk; bits are moved only.
+__global__ void __launch_bounds__(256)
+grouped_pack(const uint32_t *__restrict__ qw, const float *__restrict__ sc, uint4 *__restrict__ pw,
+             float4 *__restrict__ ps, int N, int G, long blocks) {
+  const long i = long(blockIdx.x) * 256 + threadIdx.x;
+  const long T16 = (N + 15) / 16, S4 = (G + 3) / 4;
+  if (i < blocks * 64) {  // a weight chunk
+    const long b = i / 64;
+    const int l = int(i - b * 64), c = l & 15, R = l >> 4;
+    const long s4 = b % S4, et = b / S4;
+    const long t = et % T16, e = et / T16;
+    const long n = t * 16 + c;
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const long g = s4 * 4 + q;
+      v[q] = (n < N && g < G) ? qw[((e * N + n) * G + g) * 4 + R] : 0x88888888u;
+    }
+    pw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  } else if (i < blocks * 64 + blocks * 16) {  // a scale chunk
+    const long j = i - blocks * 64;
+    const long b = j / 16;
+    const int c = int(j - b * 16);
+    const long s4 = b % S4, et = b / S4;
+    const long t = et % T16, e = et / T16;
+    const long n = t * 16 + c;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const long g = s4 * 4 + q;
+      v[q] = (n < N && g < G) ? sc[(e * N + n) * G + g] : 0.0f;
+    }
+    ps[j] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+long grouped_pack_blocks(int E, int N, int G) {
+  return long(E) * ((N + 15) / 16) * ((G + 3) / 4);
 }
 
 struct RowsPlan {
@@ -845,13 +944,9 @@ hipError_t launch_grouped(const float *X, const int32_t *token_index, const int3
   if (E > 65535) return hipErrorInvalidConfiguration;
   MfmaPlan mp;
   const int cus = compute_units();
-  if (plan_mfma(T, R, E, N, G, cus, mp)) {
-    switch (mp.MR) {
-      case 1: return run_mfma<1>(mp, X, token_index, offsets, qweight, scales, Y, T, R, E, N, G, stream);
-      case 2: return run_mfma<2>(mp, X, token_index, offsets, qweight, scales, Y, T, R, E, N, G, stream);
-      default: return run_mfma<4>(mp, X, token_index, offsets, qweight, scales, Y, T, R, E, N, G, stream);
-    }
-  }
+  if (plan_mfma(T, R, E, N, G, cus, mp))
+    return run_mfma_any(mp, X, token_index, offsets, reinterpret_cast<const uint4 *>(qweight),
+                        scales, false, Y, T, R, E, N, G, stream);
   RowsPlan rp;
   if (plan_rows(R, E, N, G, rp)) {
     switch (rp.MT) {
@@ -873,6 +968,41 @@ hipError_t launch_grouped(const float *X, const int32_t *token_index, const int3
     case 4 * 16 + 1: return run_grouped<4, 1>(p, X, token_index, offsets, qweight, scales, Y, T, R, E, N, G, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+size_t grouped_pack_bytes(int E, int N, int K) {
+  return size_t(grouped_pack_blocks(E, N, K / kGroup)) * (1024 + 256);
+}
+
+hipError_t launch_grouped_pack(const int32_t *qweight, const float *scales, void *packed, int E,
+                               int N, int K, hipStream_t stream) {
+  const int G = K / kGroup;
+  const long blocks = grouped_pack_blocks(E, N, G);
+  const long chunks = blocks * (64 + 16);
+  if ((chunks + 255) / 256 > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  uint4 *pw = static_cast<uint4 *>(packed);
+  float4 *ps = reinterpret_cast<float4 *>(pw + blocks * 64);
+  hipLaunchKernelGGL(grouped_pack, dim3(unsigned((chunks + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t *>(qweight), scales, pw, ps, N, G, blocks);
+  return hipGetLastError();
+}
+
+bool grouped_packed_supported(int T, int R, int E, int N, int K) {
+  MfmaPlan mp;
+  return plan_mfma(T, R, E, N, K / kGroup, 256, mp);
+}
+
+hipError_t launch_grouped_packed(const float *X, const int32_t *token_index,
+                                 const int32_t *offsets, const void *packed, float *Y, int T,
+                                 int R, int E, int N, int K, hipStream_t stream) {
+  const int G = K / kGroup;
+  if (E > 65535) return hipErrorInvalidConfiguration;
+  MfmaPlan mp;
+  if (!plan_mfma(T, R, E, N, G, compute_units(), mp)) return hipErrorInvalidValue;
+  const long blocks = grouped_pack_blocks(E, N, G);
+  const uint4 *pw = static_cast<const uint4 *>(packed);
+  const float *ps = reinterpret_cast<const float *>(pw + blocks * 64);
+  return run_mfma_any(mp, X, token_index, offsets, pw, ps, true, Y, T, R, E, N, G, stream);
 }
 
 }  // namespace w4a16

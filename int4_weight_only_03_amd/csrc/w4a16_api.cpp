@@ -127,6 +127,62 @@ int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+size_t w4a16_grouped_pack_bytes(int64_t E, int64_t N, int64_t K) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
+  return w4a16::grouped_pack_bytes(int(E), int(N), int(K));
+}
+
+int w4a16_grouped_pack(const int32_t *qweight, const float *scales, int64_t E, int64_t N,
+                       int64_t K, int32_t group, void *packed, size_t packed_bytes,
+                       void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (E <= 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (N == 0) return W4A16_OK;
+  if (!qweight || !scales || !packed) return W4A16_ERR_ARG;
+  if (!aligned(qweight, 16) || !aligned(scales, 4)) return W4A16_ERR_ALIGN;
+  const size_t need = w4a16::grouped_pack_bytes(int(E), int(N), int(K));
+  if (!aligned(packed, 16) || packed_bytes < need) return W4A16_ERR_ARG;
+  const size_t bq = size_t(E) * size_t(N) * size_t(K) / 2;
+  const size_t bs = size_t(E) * size_t(N) * size_t(K / W4A16_GROUP) * 4;
+  if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_grouped_pack(qweight, scales, packed, int(E), int(N), int(K),
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
+                              const int32_t *expert_offsets, const void *packed, float *Y,
+                              int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
+                              int32_t group, void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (T < 0 || R < 0 || E <= 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)
+    return W4A16_ERR_SHAPE;
+  if (R == 0 || N == 0) return W4A16_OK;
+  if (T == 0) return W4A16_ERR_ARG;
+  if (!X || !token_index || !expert_offsets || !packed || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4) || !aligned(token_index, 4) ||
+      !aligned(expert_offsets, 4))
+    return W4A16_ERR_ALIGN;
+  if (!w4a16::grouped_packed_supported(int(T), int(R), int(E), int(N), int(K)))
+    return W4A16_ERR_SHAPE;
+  const size_t bx = size_t(T) * size_t(K) * 4, by = size_t(R) * size_t(N) * 4;
+  const size_t bp = w4a16::grouped_pack_bytes(int(E), int(N), int(K));
+  const size_t bi = size_t(R) * 4, bo = size_t(E + 1) * 4;
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp) || overlaps(Y, by, token_index, bi) ||
+      overlaps(Y, by, expert_offsets, bo))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_grouped_packed(X, token_index, expert_offsets, packed, Y, int(T),
+                                              int(R), int(E), int(N), int(K),
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
   if (T <= 0 || R <= 0 || E <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)

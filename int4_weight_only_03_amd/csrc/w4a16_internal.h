@@ -49,6 +49,15 @@ hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const floa
 // which kernel launch_grouped runs for this shape: 1 matrix cores, 2 fp32
 // FMA with staged token rows, 3 fp32 FMA reading activations from memory
 int grouped_kernel(int T, int R, int E, int N, int K);
+// the packed layout of the grouped path: bytes, repack, the packed GEMM and
+// whether a shape can use it
+size_t grouped_pack_bytes(int E, int N, int K);
+hipError_t launch_grouped_pack(const int32_t *qweight, const float *scales, void *packed, int E,
+                               int N, int K, hipStream_t stream);
+bool grouped_packed_supported(int T, int R, int E, int N, int K);
+hipError_t launch_grouped_packed(const float *X, const int32_t *token_index,
+                                 const int32_t *offsets, const void *packed, float *Y, int T,
+                                 int R, int E, int N, int K, hipStream_t stream);
 hipError_t launch_grouped(const float *X, const int32_t *token_index, const int32_t *offsets,
                           const int32_t *qweight, const float *scales, float *Y, int T, int R,
                           int E, int N, int K, hipStream_t stream);

@@ -30,6 +30,10 @@ from .w4a16_ref import (  # noqa: F401
     swiglu_bound,
     compare_swiglu,
     unpack_split,
+    pack_grouped,
+    unpack_grouped,
+    TILE_ROWS,
+    STEP_GROUPS,
     SLAB,
     STAGE_GROUPS,
 )

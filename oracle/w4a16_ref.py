@@ -209,6 +209,65 @@ def unpack_split(packed: np.ndarray, N: int, K: int) -> tuple[np.ndarray, np.nda
     return qweight.view(np.int32), scales
 
 
+TILE_ROWS = 16     # grouped repack: weight rows per tile
+STEP_GROUPS = 4    # grouped repack: groups per step
+
+
+def pack_grouped(qweight: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed grouped-path layout of (qweight[E][N][K/8], scales[E][N][K/32])
+    as bytes.
+
+    For expert e, tile t (rows 16t..16t+15) and step s (groups 4s..4s+3),
+    with T16 tiles and S4 steps, block b = (e*T16 + t)*S4 + s: 16-byte chunk
+    b*64 + c + 16R holds word R of groups 4s..4s+3 (in that order) of row
+    16t + c; after all E*T16*S4*1024 such bytes, float (b*16 + c)*4 + q holds
+    the scale of group 4s + q of row 16t + c.  Rows past N and groups past G
+    hold words 0x88888888 (every nibble 8, code 0) and scale 0.0.
+    """
+    qweight = np.ascontiguousarray(qweight).view(np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=_F32)
+    E, N, G = scales.shape
+    if qweight.shape != (E, N, 4 * G):
+        raise ValueError("qweight and scales disagree")
+    T16 = -(-N // TILE_ROWS)
+    S4 = -(-G // STEP_GROUPS)
+    words = np.full((E, T16, S4, 4, TILE_ROWS, STEP_GROUPS), 0x88888888, dtype=np.uint32)
+    sc = np.zeros((E, T16, S4, TILE_ROWS, STEP_GROUPS), dtype=_F32)
+    for e in range(E):                      # plain loops: expert, row, group, word
+        for n in range(N):
+            t, c = divmod(n, TILE_ROWS)
+            for g in range(G):
+                s_, q = divmod(g, STEP_GROUPS)
+                for R in range(4):
+                    words[e, t, s_, R, c, q] = qweight[e, n, 4 * g + R]
+                sc[e, t, s_, c, q] = scales[e, n, g]
+    return np.concatenate([words.reshape(-1).view(np.uint8), sc.reshape(-1).view(np.uint8)])
+
+
+def unpack_grouped(packed: np.ndarray, E: int, N: int, K: int) -> tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack_grouped: (qweight int32 [E][N][K/8], scales fp32 [E][N][K/32])."""
+    check_k(K)
+    G = K // GROUP
+    T16 = -(-N // TILE_ROWS)
+    S4 = -(-G // STEP_GROUPS)
+    nw = E * T16 * S4 * 4 * TILE_ROWS * STEP_GROUPS
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    words = packed[:4 * nw].view(np.uint32).reshape(E, T16, S4, 4, TILE_ROWS, STEP_GROUPS)
+    sc = packed[4 * nw:4 * nw + 4 * E * T16 * S4 * TILE_ROWS * STEP_GROUPS].view(_F32).reshape(
+        E, T16, S4, TILE_ROWS, STEP_GROUPS)
+    qweight = np.zeros((E, N, 4 * G), dtype=np.uint32)
+    scales = np.zeros((E, N, G), dtype=_F32)
+    for e in range(E):
+        for n in range(N):
+            t, c = divmod(n, TILE_ROWS)
+            for g in range(G):
+                s_, q = divmod(g, STEP_GROUPS)
+                for R in range(4):
+                    qweight[e, n, 4 * g + R] = words[e, t, s_, R, c, q]
+                scales[e, n, g] = sc[e, t, s_, c, q]
+    return qweight.view(np.int32), scales
+
+
 def _operands(X, qweight, scales):
     X = np.asarray(X)
     if X.dtype != np.float32 or X.ndim != 2:

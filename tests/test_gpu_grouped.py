@@ -124,3 +124,82 @@ def test_grouped_long_k_fallback(dev):
     q, s = quantize_experts(W)
     v = oracle.compare_grouped(run(X, ti, off, q, s, dev), X, ti, off, q, s)
     assert v["ok"], v
+
+
+# ---------------------------------------------------------------- packed layout
+
+def dev_words(E, N, K, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-2**31, 2**31, size=(E, N, K // 8), dtype=np.int64).astype(np.int32)
+    s = rng.uniform(0.001, 1.0, size=(E, N, K // 32)).astype(np.float32)
+    return q, s
+
+
+@pytest.mark.parametrize("E,N,K", [(2, 20, 160), (3, 7, 96), (1, 33, 416), (4, 64, 7168)])
+def test_grouped_pack_bit_exact(dev, E, N, K):
+    say(f"grouped pack E={E} N={N} K={K}")
+    q, s = dev_words(E, N, K, E * 7 + N + K)
+    packed = binding.w4a16_grouped_pack(to_dev(q, dev), to_dev(s, dev))
+    torch.cuda.synchronize()
+    ref = oracle.pack_grouped(q, s)
+    got = packed.cpu().numpy()[:ref.size]
+    assert packed.numel() == ref.size == binding.w4a16_grouped_pack_bytes(E, N, K)
+    assert np.array_equal(got, ref)
+
+
+def test_grouped_pack_full_size_sampled(dev):
+    """The moe_decode expert shape: sampled words and scales sit at the offsets
+    the layout states (index arithmetic written out here)."""
+    wl = workloads.MOE_WORKLOADS["moe_decode"]
+    E, N, K = wl.E, wl.N, wl.K
+    say(f"grouped pack full size E={E} N={N} K={K}")
+    q, s = dev_words(E, N, K, 99)
+    packed = binding.w4a16_grouped_pack(to_dev(q, dev), to_dev(s, dev))
+    torch.cuda.synchronize()
+    p = packed.cpu().numpy()
+    G, T16, S4 = K // 32, -(-N // 16), -(-(K // 32) // 4)
+    B = E * T16 * S4
+    w32 = p[:B * 1024].view(np.uint32)
+    f32 = p[B * 1024:B * 1280].view(np.float32)
+    rng = np.random.default_rng(5)
+    qu = q.view(np.uint32)
+    for _ in range(4000):
+        e, n, g, R = rng.integers(E), rng.integers(N), rng.integers(G), rng.integers(4)
+        b = (e * T16 + n // 16) * S4 + g // 4
+        assert w32[(b * 64 + n % 16 + 16 * R) * 4 + g % 4] == qu[e, n, 4 * g + R]
+        assert f32[(b * 16 + n % 16) * 4 + g % 4] == s[e, n, g]
+
+
+@pytest.mark.parametrize("T,E,topk,N,K", [
+    (7, 5, 2, 70, 96),
+    (16, 32, 4, 64, 256),
+    (1, 64, 8, 40, 224),
+    (32, 4, 2, 96, 512),
+    (3, 4, 2, 100, 288),
+    (4, 8, 8, 128, 7168),
+])
+def test_grouped_packed_matches_unpacked(dev, T, E, topk, N, K):
+    say(f"grouped packed T={T} E={E} topk={topk} N={N} K={K}")
+    X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=T * 13 + E + N + K)
+    assert binding.w4a16_grouped_kernel(T, ti.size, E, N, K) == binding.W4A16_GROUPED_MFMA
+    q, s = quantize_experts(W)
+    packed = binding.w4a16_grouped_pack(to_dev(q, dev), to_dev(s, dev))
+    Yp = binding.w4a16_gemm_grouped_packed(to_dev(X, dev), to_dev(ti, dev), to_dev(off, dev),
+                                           packed, E, N)
+    torch.cuda.synchronize()
+    Yp = Yp.cpu().numpy()
+    Yu = run(X, ti, off, q, s, dev)
+    assert np.array_equal(Yp.view(np.uint32), Yu.view(np.uint32))
+    v = oracle.compare_grouped(Yp, X, ti, off, q, s)
+    assert v["ok"], v
+
+
+def test_grouped_packed_refuses_other_kernels(dev):
+    T, E, topk, N, K = 6, 4100, 3, 20, 96
+    X, W, ti, off = workloads.moe_case(T, E, topk, N, K, seed=21)
+    q, s = dev_words(E, N, K, 1)
+    packed = binding.w4a16_grouped_pack(to_dev(q, dev), to_dev(s, dev))
+    with pytest.raises(binding.W4A16Error) as err:
+        binding.w4a16_gemm_grouped_packed(to_dev(X, dev), to_dev(ti, dev), to_dev(off, dev),
+                                          packed, E, N)
+    assert err.value.status == 2  # W4A16_ERR_SHAPE, refused before any launch

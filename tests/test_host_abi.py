@@ -269,3 +269,42 @@ def test_grouped_kernel_choice():
     for bad in [(0, 1, 1, 8, 32), (1, 1, 0, 8, 32), (1, 1, 1, 8, 48), (1, 1, 65536, 8, 32),
                 (1, 0, 1, 8, 32)]:
         assert b.w4a16_grouped_kernel(*bad) == 0
+
+
+def test_grouped_pack_size_and_errors(lib):
+    pb = lib.w4a16_grouped_pack_bytes
+    assert pb(0, 16, 128) == 0 and pb(1, 16, 48) == 0 and pb(1, 0, 128) == 0
+    assert pb(1, 16, 128) == 1280 and pb(1, 17, 160) == 2 * 2 * 1280
+    assert pb(32, 1024, 7168) == 32 * 64 * 56 * 1280
+    P_ = BASE + (5 << 32)
+    need = pb(3, 40, 224)
+    pack = lambda q, s, e, n, k, p, nb, group=32: lib.w4a16_grouped_pack(q, s, e, n, k, group, p,
+                                                                         nb, None)
+    assert pack(Q_, S_, 3, 40, 224, P_, need - 1) == ARG
+    assert pack(Q_, S_, 3, 40, 224, None, need) == ARG
+    assert pack(Q_, S_, 3, 40, 224, P_ + 8, need) == ARG   # packed not 16-byte aligned
+    assert pack(Q_ + 4, S_, 3, 40, 224, P_, need) == ALIGN
+    assert pack(Q_, S_, 3, 40, 224, Q_, need) == ARG       # overlaps qweight
+    assert pack(Q_, S_, 3, 40, 48, P_, need) == SHAPE
+    assert pack(Q_, S_, 0, 40, 224, P_, need) == ARG
+    assert pack(Q_, S_, 65536, 40, 224, P_, need) == SHAPE
+    assert pack(Q_, S_, 3, 40, 224, P_, need, group=64) == ARG
+    assert pack(None, None, 3, 0, 224, None, 0) == OK      # N == 0: nothing to do
+
+
+def test_grouped_packed_gemm_errors(lib):
+    I_, O_, P_ = BASE + (6 << 32), BASE + (7 << 32), BASE + (5 << 32)
+    g = lambda x, p, y, t=16, r=64, e=32, n=64, k=256, group=32: lib.w4a16_gemm_grouped_packed(
+        x, I_, O_, p, y, t, r, e, n, k, group, None)
+    assert g(X_, P_, Y_, e=4100) == SHAPE                 # not a matrix-core shape
+    assert g(X_, P_, Y_, k=40992, e=2) == SHAPE           # K too long to stage
+    assert g(X_, P_ + 4, Y_) == ALIGN
+    assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(None, P_, Y_) == ARG
+    assert g(X_, None, Y_) == ARG
+    assert g(X_, P_, X_ + 64) == ARG                      # Y overlaps X
+    assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
+    assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_, Y_, group=16) == ARG
+    assert g(X_, P_, Y_, t=0) == ARG                      # slots but no tokens
+    assert g(None, None, None, r=0) == OK
