@@ -46,14 +46,18 @@ FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "int4_weight_only_03_amd/csrc/"
-PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5}
+PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5,
+              "decode-packed": 6}
 SPLIT_PATHS = ("split", "packed")
+# paths whose products are fp16 matrix instructions on two activation limbs
+LIMB_PATHS = ("split", "packed", "decode-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_common.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
-                "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"]}
+                "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
+                "decode-packed": ["packed_gemv.hip", "gemv_common.h", "limbs.h"]}
 
 
 def source_hash(path: str) -> str:
@@ -260,6 +264,20 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         def step(i):
             x, _, _, y = sets[i % copies]
             pkg.w4a16_gemm_split_packed(x, packs[i % copies], wl.N, y, workspace=ws)
+    elif path == "decode-packed":
+        # the one-time repack into the grouped layout (one expert), timed on its own
+        packs = [pkg.w4a16_grouped_pack(q[None], s[None]) for (_, q, s, _) in sets]
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        pkg.w4a16_grouped_pack(sets[0][1][None], sets[0][2][None], packs[0])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        repack_ms = ev0.elapsed_time(ev1)
+
+        def step(i):
+            x, _, _, y = sets[i % copies]
+            pkg.w4a16_gemm_decode_packed(x, packs[i % copies], wl.N, y)
     elif path == "swiglu":
         ys = [torch.empty((wl.M, wl.N // 2), dtype=torch.float32, device=dev)
               for _ in range(copies)]
@@ -281,8 +299,8 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
     value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
-    split = path in SPLIT_PATHS
-    # the split path issues fp16 matrix instructions: its compute roof is the fp16 peak
+    split = path in LIMB_PATHS
+    # the limb paths issue fp16 matrix instructions: their compute roof is the fp16 peak
     peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
     if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -425,7 +443,7 @@ def main():
         value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup, path)
         # arithmetic type: fp32 FMA/MFMA, or fp16 matrix products of two fp16
         # activation limbs and exact weight codes with fp32 accumulation
-        dtype = "f16x2-limb/f32-acc" if path in SPLIT_PATHS else "f32"
+        dtype = "f16x2-limb/f32-acc" if path in LIMB_PATHS else "f32"
         line = {
             "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

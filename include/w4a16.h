@@ -196,6 +196,27 @@ int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
                               int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
                               int32_t group, void *stream);
 
+/*
+ * Decode GEMV on packed weights: Y[M][N] = X[M][K] . dequant(W)^T for
+ * 1 <= M <= 4, W packed once by w4a16_grouped_pack(qweight, scales, 1, N, K,
+ * ...) (a single expert).  The arithmetic of w4a16_gemm_split (exact weight
+ * codes, two fp16 limbs of each prescaled activation, fp32 accumulation; a
+ * row of X holding Inf or NaN gives NaN in that row of Y), within the
+ * tolerance of w4a16_gemm.  The pages' decode steps are memory-bound GEMVs;
+ * with the packed layout every weight load reads a contiguous kilobyte.  One
+ * workgroup per 16 rows of W splits K over its waves and adds their partial
+ * sums in a fixed order (deterministic).  X, packed (16-byte aligned) and Y
+ * are DEVICE memory; Y must not overlap X or packed.  M == 0 or N == 0 is a
+ * no-op; M > 4, or a K whose activation limbs (4*M*K bytes) do not fit the
+ * kernel's LDS budget (w4a16_decode_packed_supported), is W4A16_ERR_SHAPE;
+ * otherwise errors as w4a16_gemm.
+ */
+int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                             int64_t K, int32_t group, void *stream);
+
+/* 1 if w4a16_gemm_decode_packed takes M rows with this K, else 0.  Host only. */
+int w4a16_decode_packed_supported(int64_t M, int64_t K);
+
 /* Kernels behind w4a16_gemm_grouped. */
 #define W4A16_GROUPED_MFMA 1  /* matrix cores, split-path arithmetic; up to 4096 experts
                                  and the token rows of a slot chunk staged in LDS */

@@ -67,6 +67,9 @@ _SIGS = {
                                 ctypes.c_int),
     "w4a16_grouped_kernel": ([ctypes.c_int64] * 5, ctypes.c_int),
     "w4a16_grouped_pack_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
+    "w4a16_decode_packed_supported": ([ctypes.c_int64] * 2, ctypes.c_int),
+    "w4a16_gemm_decode_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
+                                 [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_grouped_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                             ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                             ctypes.c_void_p], ctypes.c_int),
@@ -270,6 +273,34 @@ def w4a16_gemm_grouped_packed(X, token_index, expert_offsets, packed, E: int, N:
                                           _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_grouped_packed")
+    return Y
+
+
+def w4a16_decode_packed_supported(M: int, K: int) -> bool:
+    return bool(load().w4a16_decode_packed_supported(M, K))
+
+
+def w4a16_gemm_decode_packed(X, packed, N: int, Y=None, stream=None):
+    """Decode GEMV (M <= 4) on weights from w4a16_grouped_pack of one expert
+    ([1][N][K/8] qweight, [1][N][K/32] scales), N output rows."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    packed = _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    M, K = X.shape
+    if packed.numel() < w4a16_grouped_pack_bytes(1, N, K):
+        raise ValueError("packed buffer smaller than w4a16_grouped_pack_bytes(1, N, K)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    st = load().w4a16_gemm_decode_packed(X.data_ptr(), packed.data_ptr(), Y.data_ptr(), M, N, K,
+                                         GROUP, _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_decode_packed")
     return Y
 
 

@@ -12,6 +12,7 @@
 #include "../../include/w4a16.h"
 #include "w4a16_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -180,6 +181,29 @@ int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
   hipError_t e = w4a16::launch_grouped_packed(X, token_index, expert_offsets, packed, Y, int(T),
                                               int(R), int(E), int(N), int(K),
                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_decode_packed_supported(int64_t M, int64_t K) {
+  if (M < 1 || K <= 0 || K % W4A16_GROUP != 0 || K > W4A16_MAX_K) return 0;
+  return w4a16::decode_packed_supported(int(std::min<int64_t>(M, 5)), int(K)) ? 1 : 0;
+}
+
+int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                             int64_t K, int32_t group, void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!w4a16::decode_packed_supported(int(std::min<int64_t>(M, 5)), int(K))) return W4A16_ERR_SHAPE;
+  if (!X || !packed || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4)) return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(M) * size_t(K) * 4, by = size_t(M) * size_t(N) * 4;
+  const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K),
+                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

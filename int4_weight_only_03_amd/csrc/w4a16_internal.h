@@ -49,6 +49,10 @@ hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const floa
 // which kernel launch_grouped runs for this shape: 1 matrix cores, 2 fp32
 // FMA with staged token rows, 3 fp32 FMA reading activations from memory
 int grouped_kernel(int T, int R, int E, int N, int K);
+// decode GEMV (M <= 4) on weights packed by the grouped repack (one expert)
+bool decode_packed_supported(int M, int K);
+hipError_t launch_decode_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
+                                hipStream_t stream);
 // the packed layout of the grouped path: bytes, repack, the packed GEMM and
 // whether a shape can use it
 size_t grouped_pack_bytes(int E, int N, int K);

@@ -308,3 +308,21 @@ def test_grouped_packed_gemm_errors(lib):
     assert g(X_, P_, Y_, group=16) == ARG
     assert g(X_, P_, Y_, t=0) == ARG                      # slots but no tokens
     assert g(None, None, None, r=0) == OK
+
+
+def test_decode_packed_errors(lib):
+    P_ = BASE + (5 << 32)
+    g = lambda x, p, y, m=1, n=64, k=256, group=32: lib.w4a16_gemm_decode_packed(
+        x, p, y, m, n, k, group, None)
+    assert g(X_, P_, Y_, m=5) == SHAPE
+    assert g(X_, P_, Y_, k=38176) == SHAPE
+    assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_ + 4, Y_) == ALIGN
+    assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(None, P_, Y_) == ARG
+    assert g(X_, P_, X_ + 64) == ARG                      # Y overlaps X
+    assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
+    assert g(X_, P_, Y_, group=16) == ARG
+    assert g(None, None, None, m=0) == OK
+    assert lib.w4a16_decode_packed_supported(1, 7168) == 1
+    assert lib.w4a16_decode_packed_supported(0, 7168) == 0
