@@ -217,6 +217,34 @@ int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64
 /* 1 if w4a16_gemm_decode_packed takes M rows with this K, else 0.  Host only. */
 int w4a16_decode_packed_supported(int64_t M, int64_t K);
 
+/*
+ * Small-M GEMM on packed weights: Y[M][N] = X[M][K] . dequant(W)^T for
+ * 1 <= M <= W4A16_SMALL_MAX_M, W packed once by w4a16_grouped_pack(qweight,
+ * scales, 1, N, K, ...) (a single expert).  For the pages' tree-verification
+ * batches (a few dozen draft tokens scored against each weight in one pass).
+ * The arithmetic of w4a16_gemm_split (exact weight codes, two fp16 limbs of
+ * each activation, fp32 accumulation; a row of X holding Inf or NaN gives NaN
+ * in that row of Y), within the tolerance of w4a16_gemm; each row's power of
+ * two is taken per K slice.  The K range may be split over workgroups; their
+ * partial results go to `workspace` and are added in a fixed order
+ * (deterministic).  workspace: DEVICE memory of at least
+ * w4a16_small_packed_workspace_bytes(M, N, K) bytes, 256-byte aligned, not
+ * overlapping X, packed or Y; it may be NULL when that size is 0.  Its contents
+ * on entry do not matter and are clobbered.  X, packed (16-byte aligned) and Y
+ * are DEVICE memory; Y must not overlap X or packed.  M == 0 or N == 0 is a
+ * no-op; M > W4A16_SMALL_MAX_M is W4A16_ERR_SHAPE; a missing, misaligned, too
+ * small or overlapping workspace is W4A16_ERR_ARG; otherwise errors as
+ * w4a16_gemm.
+ */
+#define W4A16_SMALL_MAX_M 64
+int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                            int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Workspace bytes w4a16_gemm_small_packed needs (0 when K is not split, or
+ * when the shape is not accepted).  Host only. */
+size_t w4a16_small_packed_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* Kernels behind w4a16_gemm_grouped. */
 #define W4A16_GROUPED_MFMA 1  /* matrix cores, split-path arithmetic; up to 4096 experts
                                  and the token rows of a slot chunk staged in LDS */

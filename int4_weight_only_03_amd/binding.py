@@ -70,6 +70,10 @@ _SIGS = {
     "w4a16_decode_packed_supported": ([ctypes.c_int64] * 2, ctypes.c_int),
     "w4a16_gemm_decode_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
                                  [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_small_packed_workspace_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
+    "w4a16_gemm_small_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
+                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p], ctypes.c_int),
     "w4a16_grouped_pack": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                             ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                             ctypes.c_void_p], ctypes.c_int),
@@ -301,6 +305,41 @@ def w4a16_gemm_decode_packed(X, packed, N: int, Y=None, stream=None):
                                          GROUP, _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_decode_packed")
+    return Y
+
+
+def w4a16_small_packed_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().w4a16_small_packed_workspace_bytes(M, N, K))
+
+
+def w4a16_gemm_small_packed(X, packed, N: int, Y=None, workspace=None, stream=None):
+    """Small-M GEMM (M <= 64) on weights from w4a16_grouped_pack of one expert
+    ([1][N][K/8] qweight, [1][N][K/32] scales), N output rows; `workspace` is a
+    uint8 device tensor of at least w4a16_small_packed_workspace_bytes(M, N, K)
+    bytes (allocated here if None)."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    packed = _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    M, K = X.shape
+    if packed.numel() < w4a16_grouped_pack_bytes(1, N, K):
+        raise ValueError("packed buffer smaller than w4a16_grouped_pack_bytes(1, N, K)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    need = w4a16_small_packed_workspace_bytes(M, N, K) if M and N else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    workspace = _dev(workspace, torch.uint8, "workspace")
+    st = load().w4a16_gemm_small_packed(X.data_ptr(), packed.data_ptr(), Y.data_ptr(), M, N, K,
+                                        GROUP, workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_small_packed")
     return Y
 
 

@@ -207,6 +207,37 @@ int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+size_t w4a16_small_packed_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > W4A16_SMALL_MAX_M || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
+  return w4a16::small_packed_workspace_bytes(int(M), int(N), int(K));
+}
+
+int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                            int64_t K, int32_t group, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_SMALL_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!X || !packed || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4)) return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(M) * size_t(K) * 4, by = size_t(M) * size_t(N) * 4;
+  const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
+  const size_t need = w4a16::small_packed_workspace_bytes(int(M), int(N), int(K));
+  if (need > 0) {
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W4A16_ERR_ARG;
+    if (overlaps(workspace, need, X, bx) || overlaps(workspace, need, packed, bp) ||
+        overlaps(workspace, need, Y, by))
+      return W4A16_ERR_ARG;
+  }
+  hipError_t e = w4a16::launch_small_packed(X, packed, Y, int(M), int(N), int(K), workspace,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
   if (T <= 0 || R <= 0 || E <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)

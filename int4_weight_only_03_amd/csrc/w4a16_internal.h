@@ -53,6 +53,12 @@ int grouped_kernel(int T, int R, int E, int N, int K);
 bool decode_packed_supported(int M, int K);
 hipError_t launch_decode_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
                                 hipStream_t stream);
+// small-M GEMM (1 <= M <= 64) on weights packed by the grouped repack (one
+// expert); workspace: the split-K partials (0 bytes when K is not split)
+bool small_packed_supported(int M);
+size_t small_packed_workspace_bytes(int M, int N, int K);
+hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
+                               void *workspace, hipStream_t stream);
 // the packed layout of the grouped path: bytes, repack, the packed GEMM and
 // whether a shape can use it
 size_t grouped_pack_bytes(int E, int N, int K);

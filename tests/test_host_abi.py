@@ -326,3 +326,31 @@ def test_decode_packed_errors(lib):
     assert g(None, None, None, m=0) == OK
     assert lib.w4a16_decode_packed_supported(1, 7168) == 1
     assert lib.w4a16_decode_packed_supported(0, 7168) == 0
+
+
+def test_small_packed_errors(lib):
+    P_, W_ = BASE + (5 << 32), BASE + (6 << 32)
+    need = lib.w4a16_small_packed_workspace_bytes(64, 4096, 7168)
+    # 16 groups of 256 columns x 2 chunks of 32 rows x 8 K slices of 7 steps
+    # (896 k): 256 workgroups, 8 partial results
+    assert need == 8 * 64 * 4096 * 4
+    assert lib.w4a16_small_packed_workspace_bytes(4, 16, 128) == 0    # one slice: no partials
+    assert lib.w4a16_small_packed_workspace_bytes(65, 4096, 7168) == 0
+    assert lib.w4a16_small_packed_workspace_bytes(8, 4096, 48) == 0
+    g = lambda x, p, y, m=64, n=4096, k=7168, group=32, ws=W_, wsb=need: \
+        lib.w4a16_gemm_small_packed(x, p, y, m, n, k, group, ws, wsb, None)
+    assert g(X_, P_, Y_, m=65) == SHAPE
+    assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_, Y_, group=16) == ARG
+    assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(X_, P_ + 4, Y_) == ALIGN
+    assert g(None, P_, Y_) == ARG
+    assert g(X_, P_, X_ + 64) == ARG                      # Y overlaps X
+    assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
+    assert g(X_, P_, Y_, ws=None) == ARG                  # partials need a workspace
+    assert g(X_, P_, Y_, ws=W_ + 16) == ARG               # not 256-byte aligned
+    assert g(X_, P_, Y_, wsb=need - 4) == ARG             # too small
+    assert g(X_, P_, Y_, ws=X_) == ARG                    # overlaps X
+    assert g(X_, P_, Y_, ws=Y_) == ARG                    # overlaps Y
+    assert g(None, None, None, m=0) == OK
+    assert g(None, None, None, n=0) == OK
