@@ -56,7 +56,7 @@ SPLIT_PATHS = ("split", "packed")
 # paths whose products are fp16 matrix instructions on two activation limbs
 LIMB_PATHS = ("split", "packed", "decode-packed", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
-PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
+PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_common.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
@@ -320,8 +320,12 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     gbs = B / (ms_per_step * 1e-3) / 1e9
     tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
     value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
-    split = path in LIMB_PATHS
-    # the limb paths issue fp16 matrix instructions: their compute roof is the fp16 peak
+    resolved = path if path != "auto" else \
+        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)]
+    # the limb paths issue fp16 matrix instructions (so does the GEMV path's
+    # matrix-core kernel): their compute roof is the fp16 peak
+    split = path in LIMB_PATHS or (
+        resolved == "gemv" and pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == pkg.W4A16_GEMV_MFMA)
     peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
     if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -329,8 +333,6 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     else:
         roof = {"bound": "mfma", "achieved": tfs, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": tfs / peak_tf}
-    resolved = path if path != "auto" else \
-        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)]
     roof["traffic"] = measured_traffic(name, resolved)
     med = statistics.median(per_launch_ms)
     extra = {
@@ -347,6 +349,7 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "repack_ms_one_time": repack_ms,
         "fp32_frac": tfs / FP32_PEAK_TFLOPS,
+        "limb_arithmetic": split,
     }
     y0 = (ys[0] if path == "swiglu" else sets[0][3]).cpu().numpy()
     return value, unit, ms_per_step, roof, extra, (X, W, y0)
@@ -464,7 +467,7 @@ def main():
         value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup, path)
         # arithmetic type: fp32 FMA/MFMA, or fp16 matrix products of two fp16
         # activation limbs and exact weight codes with fp32 accumulation
-        dtype = "f16x2-limb/f32-acc" if path in LIMB_PATHS else "f32"
+        dtype = "f16x2-limb/f32-acc" if extra["limb_arithmetic"] else "f32"
         line = {
             "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

@@ -64,7 +64,9 @@ extern "C" {
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
-#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV, x in VGPRs */
+#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV; for M <= 2 and
+                                 K <= 8192 on the 4x4x4 fp16 matrix instructions
+                                 (w4a16_gemv_kernel) */
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
 #define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
                                  exact (q - 8) codes and two fp16 limbs of each activation */
@@ -255,6 +257,22 @@ size_t w4a16_small_packed_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * N x K expert shape (one of W4A16_GROUPED_*), or 0 for a shape it refuses or
  * treats as a no-op.  Host only; no GPU use. */
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
+
+/* Kernels behind W4A16_PATH_GEMV. */
+#define W4A16_GEMV_MFMA 1     /* M <= 2, K <= 8192: v_mfma_f32_4x4x4_16b_f16 on exact weight
+                                 codes (nibble - 8) and two fp16 limbs of each activation; every
+                                 group of 32 activations is scaled by a power of two (max |x|
+                                 into [2^14, 2^15)) before the split, so the limbs hold 22
+                                 significant bits; products exact in fp32, fp32 accumulation,
+                                 one fp32 multiply per (row, group) applies scale * 2^-e */
+#define W4A16_GEMV_FMA 2      /* otherwise: one fp32 FMA per weight, activations in VGPRs */
+
+/* The kernel W4A16_PATH_GEMV runs for an M x N x K shape (one of W4A16_GEMV_*), or 0
+ * for a shape w4a16_gemm refuses.  Host only; no GPU use.  (Decode GEMV: the pages'
+ * path for memory-bound MoE inference, "The Quiet Commit: How a Single Plan Update
+ * Closed Phase 3 of a Native DDTree Inference Engine", section "Input and Output
+ * Knowledge".) */
+int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
 
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);

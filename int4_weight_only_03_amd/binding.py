@@ -66,6 +66,7 @@ _SIGS = {
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
                                 ctypes.c_int),
     "w4a16_grouped_kernel": ([ctypes.c_int64] * 5, ctypes.c_int),
+    "w4a16_gemv_kernel": ([ctypes.c_int64] * 3, ctypes.c_int),
     "w4a16_grouped_pack_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
     "w4a16_decode_packed_supported": ([ctypes.c_int64] * 2, ctypes.c_int),
     "w4a16_gemm_decode_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
@@ -213,6 +214,15 @@ def w4a16_gemm_path(X, qweight, scales, Y=None, path: int = W4A16_PATH_AUTO, str
 W4A16_GROUPED_MFMA = 1
 W4A16_GROUPED_ROWS = 2
 W4A16_GROUPED_GEMV = 3
+
+
+W4A16_GEMV_MFMA = 1
+W4A16_GEMV_FMA = 2
+
+
+def w4a16_gemv_kernel(M: int, N: int, K: int) -> int:
+    """Kernel of the GEMV path for this shape (W4A16_GEMV_*), 0 if the shape is refused."""
+    return load().w4a16_gemv_kernel(M, N, K)
 
 
 def w4a16_grouped_kernel(T: int, R: int, E: int, N: int, K: int) -> int:

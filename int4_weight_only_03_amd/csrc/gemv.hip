@@ -425,6 +425,8 @@ hipError_t launch(const float *X, const int32_t *qweight, const float *scales, f
 
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream) {
+  if (gemv_mfma_supported(M, K))  // matrix-core decode GEMV (gemv_mfma.hip)
+    return launch_gemv_mfma(X, qweight, scales, Y, M, N, K, stream);
   return launch<false>(X, qweight, scales, Y, M, N, K, stream);
 }
 

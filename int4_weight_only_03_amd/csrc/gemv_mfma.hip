@@ -1,0 +1,237 @@
+// Decode GEMV (M <= 2) on the 4x4x4 fp16 matrix instructions.
+//
+// The decode path exists for memory-bound MoE inference and aims at the HBM
+// bandwidth peak ("The Quiet Commit: How a Single Plan Update Closed Phase 3
+// of a Native DDTree Inference Engine", sections "Input and Output Knowledge"
+// and "The Thinking Process"); unpacking must not eat the bandwidth that
+// 4-bit storage saves ("The Silence of Success: A Single Line That Speaks
+// Volumes", section "Assumptions Embedded in the Code").  On gfx950 an fp32
+// FMA per weight plus its conversion left the kernel bound by VALU issue
+// even with every operand in cache; here the products go to the matrix
+// cores and the VALU only converts nibbles (about 1.1 operations per weight).
+//
+// Arithmetic (the split path's, per group instead of per row):
+//  * Each group of 32 activations is scaled by 2^e so that its largest
+//    magnitude lies in [2^14, 2^15), and split into fp16 limbs hi = f16(x'),
+//    lo = f16((x' - hi) * 2^11); x' = hi + 2^-11 lo to 22 significant bits
+//    for every activation down to 2^-28 of the group maximum, and to an
+//    absolute 2^-50 of that maximum below it (lo carries 2^11 so that it
+//    stays out of the fp16 subnormals).  Products of a limb and an exact
+//    fp16 weight code (q - 8) are exact in fp32.
+//  * v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products.  Block b
+//    of a wave is group g = 16*wave + b.  Its A operand (4 x 4) holds the limb
+//    rows (hi and lo of each activation row), its B operand (4 x 4) four W
+//    rows; eight instructions cover the group's 32 k, accumulating from zero.
+//    Lane 4b + j is W row j as B operand and receives D[.][j] (the limb sums
+//    of that row), so the lane that loaded a row's 16 bytes and scale also
+//    applies the scale: y += (s * 2^-e) * (D_hi + 2^-11 D_lo), one group at a time,
+//    so no group ever mixes with another's scale.
+//  * Sums over groups: 4-lane strides inside 16-lane rows by DPP rotation,
+//    across the wave's rows by permlane swaps, across waves in LDS in wave
+//    order.  No atomics: every output is summed in a fixed order.
+//
+// Loads: each lane first loads its 8 activations (the group's quarter j) and
+// then all of its weight and scale loads, so the weights stream while the
+// activations are split.  One workgroup covers 4R rows and all groups (one
+// wave per 16 groups, K <= 8192), about one workgroup per compute unit.
+
+#include "w4a16_internal.h"
+#include "gemv_common.h"
+#include "limbs.h"
+
+#include <algorithm>
+
+namespace w4a16 {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMxMaxGroups = 256;  // 16 waves of 16 groups: K <= 8192
+
+// Limbs of 8 prescaled activations a = x[k..k+3], c = x[k+4..k+7] in the
+// order the nibble conversion produces (x0 x4 x1 x5 x2 x6 x3 x7):
+// hi = f16(x * 2^e), lo = f16((x * 2^e - hi) * 2^11).
+__device__ __forceinline__ void split_block_wide(const float4 a, const float4 c, int e, half8_t &h,
+                                                 half8_t &l) {
+  const float v[8] = {a.x, c.x, a.y, c.y, a.z, c.z, a.w, c.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xs = ldexpf(v[i], e);
+    const _Float16 hv = (_Float16)xs;
+    h[i] = hv;
+    l[i] = (_Float16)((xs - (float)hv) * 2048.0f);  // xs - hv is exact; * 2^11 exact
+  }
+}
+
+// LDS: per wave [16 groups][2*MT limb rows][4 quarters] of 8 fp16 (at most
+// 64 KB).  Once a wave has read its limbs back, the start of its region holds
+// its [MT][4R] partial sums.
+constexpr size_t mx_wave_lds(int MT) { return size_t(16) * 2 * MT * 64; }
+static_assert(mx_wave_lds(1) >= 1 * 4 * 8 * sizeof(float), "partials fit the limb region");
+
+template <int MT, int R>
+__global__ void __launch_bounds__(1024)
+gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
+        float *__restrict__ Y, int M, int N, int G) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = lane >> 2, j = lane & 3;
+  const int g = wave * 16 + b;
+  const bool gv = g < G;
+  const int gc = gv ? g : G - 1;  // clamped: every load stays in bounds
+  const long K = long(G) * kGroup;
+  const long rowbase = long(blockIdx.x) * (4 * R);
+
+  // activations first (quarter j of group gc for each row), then the weights
+  float4 xa[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mr = m < M ? m : 0;
+    const float4 *xp = reinterpret_cast<const float4 *>(X + mr * K + long(gc) * kGroup + 8 * j);
+    xa[m][0] = xp[0];
+    xa[m][1] = xp[1];
+  }
+  uint4 w[R];
+  float s[R];
+  {
+    // block-relative 32-bit offsets; rows past N read the last row
+    const uint4 *qb = qw + rowbase * G;
+    const float *sb = sc + rowbase * G;
+    const int nmax = int(std::min(long(N) - 1 - rowbase, long(4 * R - 1)));
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int off = std::min(4 * q + j, nmax) * G + gc;
+      w[q] = load_stream16(qb + off);
+      s[q] = load_stream4(sb + off);
+    }
+  }
+
+  // group maxima (the 4 lanes of a quad hold one group), exponents, limbs
+  half8_t *lb = reinterpret_cast<half8_t *>(smem + wave * mx_wave_lds(MT));
+  float inv[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (!gv) xa[m][0] = xa[m][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a0 = xa[m][0], a1 = xa[m][1];
+    float mx = fmaxf(fmaxf(fmaxf(fabsf(a0.x), fabsf(a0.y)), fmaxf(fabsf(a0.z), fabsf(a0.w))),
+                     fmaxf(fmaxf(fabsf(a1.x), fabsf(a1.y)), fmaxf(fabsf(a1.z), fabsf(a1.w))));
+    // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad gets the group maximum
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xf, 0xf, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xf, 0xf, false)));
+    // e in [-113, 126]: 2^-e is a normal fp32 number.  Groups below 2^-112
+    // keep fewer limb bits; their absolute error stays below 2^-130.
+    const int e = std::min(row_exponent(mx), 126);
+    inv[m] = __int_as_float((127 - e) << 23);
+    half8_t h, l;
+    split_block_wide(a0, a1, e, h, l);
+    lb[(b * 2 * MT + 2 * m) * 4 + j] = h;
+    lb[(b * 2 * MT + 2 * m + 1) * 4 + j] = l;
+  }
+  // the wave reads back what its own lanes wrote (LDS operations of one wave
+  // complete in order)
+  __builtin_amdgcn_wave_barrier();
+  half8_t a[4];  // A operand: limb row j (MT = 1: rows 2, 3 are zero)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (j < 2 * MT) a[c] = lb[(b * 2 * MT + j) * 4 + c];
+    else a[c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  float acc[MT][R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+    floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // word c: k = 8c..8c+7 in the order of split_block
+      const half8_t bw = nibbles_to_f16(u[c]);
+      const half4_t a0 = {a[c][0], a[c][1], a[c][2], a[c][3]};
+      const half4_t a1 = {a[c][4], a[c][5], a[c][6], a[c][7]};
+      const half4_t b0 = {bw[0], bw[1], bw[2], bw[3]};
+      const half4_t b1 = {bw[4], bw[5], bw[6], bw[7]};
+      d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float sp = gv ? s[q] * inv[m] : 0.0f;  // exact: a power-of-two factor
+      acc[m][q] = sp * fmaf(d[2 * m + 1], 0x1p-11f, d[2 * m]);
+    }
+  }
+
+  // sum over the wave's groups: lanes with equal j
+  float *red = reinterpret_cast<float *>(smem + wave * mx_wave_lds(MT));  // this wave's own region
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      float v = acc[m][q];
+      v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+      v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+      const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(h32[0]) + __uint_as_float(h32[1]);
+      const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
+      if (lane < 4) red[m * (4 * R) + 4 * q + lane] = v;
+    }
+  __syncthreads();
+  for (int o = threadIdx.x; o < MT * 4 * R; o += blockDim.x) {
+    const int m = o / (4 * R), r = o - m * (4 * R);
+    float v = 0.0f;
+    for (int ww = 0; ww < int(blockDim.x >> 6); ++ww)
+      v += reinterpret_cast<const float *>(smem + ww * mx_wave_lds(MT))[m * (4 * R) + r];
+    const long n = rowbase + r;
+    if (m < M && n < N) Y[long(m) * N + n] = v;
+  }
+}
+
+template <int MT, int R>
+hipError_t run_mx(const float *X, const int32_t *qw, const float *sc, float *Y, int M, int N,
+                  int G, hipStream_t stream) {
+  const int waves = (G + 15) / 16;
+  const int blocks = int((long(N) + 4 * R - 1) / (4 * R));
+  hipLaunchKernelGGL((gemv_mx<MT, R>), dim3(blocks), dim3(waves * 64), waves * mx_wave_lds(MT),
+                     stream, X, reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc, float *Y, int M,
+                       int N, int G, hipStream_t stream) {
+  switch (R) {
+    case 8: return run_mx<MT, 8>(X, qw, sc, Y, M, N, G, stream);
+    case 4: return run_mx<MT, 4>(X, qw, sc, Y, M, N, G, stream);
+    case 2: return run_mx<MT, 2>(X, qw, sc, Y, M, N, G, stream);
+    default: return run_mx<MT, 1>(X, qw, sc, Y, M, N, G, stream);
+  }
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(int M, int K) {
+  return M >= 1 && M <= 2 && K / kGroup <= kMxMaxGroups;
+}
+
+// Quads of rows per lane: the most that still leaves at least 224 workgroups
+// (most of the 256 compute units busy), at least one.
+int gemv_mfma_quads(int N) {
+  int R = 1;
+  for (int r : {8, 4, 2})
+    if ((long(N) + 4 * r - 1) / (4 * r) >= 224) {
+      R = r;
+      break;
+    }
+  return R;
+}
+
+hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                            int M, int N, int K, hipStream_t stream) {
+  if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  const int R = gemv_mfma_quads(N);
+  return M == 1 ? dispatch_mx<1>(R, X, qweight, scales, Y, M, N, G, stream)
+                : dispatch_mx<2>(R, X, qweight, scales, Y, M, N, G, stream);
+}
+
+}  // namespace w4a16

@@ -238,6 +238,12 @@ int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
+  return w4a16::gemv_mfma_supported(int(M), int(K)) ? W4A16_GEMV_MFMA : W4A16_GEMV_FMA;
+}
+
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
   if (T <= 0 || R <= 0 || E <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (T > W4A16_MAX_M || R > W4A16_MAX_M || E > 65535 || N > W4A16_MAX_N || K > W4A16_MAX_K)

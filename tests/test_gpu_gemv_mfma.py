@@ -1,0 +1,149 @@
+"""GPU parity of the matrix-core decode GEMV (W4A16_GEMV_MFMA: M <= 2, K <= 8192).
+
+The kernel computes with exact fp16 weight codes and two fp16 limbs of each
+activation group scaled by a power of two; every output must still satisfy
+|Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6 against the fp64 oracle.  Inputs
+are seeded synthetic draws quantized by the oracle; nothing expected comes from
+the HIP path.  The cases cover groups that do not fill a wave (K not a multiple
+of 512), ragged N at every rows-per-lane setting, both row counts, the largest
+K the kernel takes and the first K it hands to the fp32 kernel, groups of very
+different magnitudes, integer inputs that must be exact, run-to-run
+determinism, power-of-two equivariance, writes confined to Y, and non-finite
+activations.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_only_03_amd import binding  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run(X, qw, sc, dev, Y=None):
+    Y = binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y,
+                                path=binding.W4A16_PATH_GEMV)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def check(Y, X, qw, sc, what):
+    v = oracle.compare(Y, X, qw, sc)
+    say(f"{what}: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], (what, v)
+
+
+SHAPES = [
+    # (N, K): G = K/32 groups; 16 groups per wave; rows per lane 1..8 follow N
+    (1, 32), (3, 96), (5, 256), (33, 2080), (257, 512), (300, 8192), (903, 1024),
+    (4097, 224), (4096, 7168), (7168, 2048),
+]
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_shapes_against_oracle(dev, M, N, K):
+    say(f"gemv_mfma M={M} N={N} K={K}")
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_MFMA
+    X, W = workloads.random_case(M, N, K, seed=N * 7 + K + M)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"mfma {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_first_k_past_the_kernel_uses_fp32(dev, M):
+    N, K = 70, 8192 + 32
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_FMA
+    X, W = workloads.random_case(M, N, K, seed=5)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"fp32 kernel {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_group_magnitudes_far_apart(dev, M):
+    # each group of X at its own power of two (2^-100 .. 2^100), some groups zero,
+    # some with subnormal entries, some spanning 2^26 inside the group
+    rng = np.random.default_rng(11)
+    N, K = 130, 4096
+    G = K // 32
+    X = rng.standard_normal((M, K))
+    exps = rng.integers(-100, 101, (M, G))
+    X = X * np.repeat(np.exp2(exps.astype(np.float64)), 32, axis=1)
+    X[:, 32 * 3:32 * 4] = 0.0
+    X[0, 32 * 5:32 * 6] = rng.standard_normal(32) * 1e-42  # fp32 subnormals
+    X[0, 32 * 7:32 * 8] *= np.exp2(-rng.integers(0, 27, 32).astype(np.float64))
+    X = X.astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"far-apart groups M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 7168), (2, 77, 2080), (2, 4096, 8192)])
+def test_integer_inputs_exact(dev, M, N, K):
+    # integer activations in [-8, 8] and one power-of-two scale: every partial
+    # sum is an exact fp32 integer multiple, so any order gives the oracle's value
+    X, nib = workloads.integer_case(M, N, K, seed=K + N + M)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), dtype=np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_deterministic_and_scale_equivariant(dev, M):
+    X, W = workloads.random_case(M, 1000, 7168, seed=78)
+    qw, sc = oracle.quantize(W)
+    a = run(X, qw, sc, dev)
+    b = run(X, qw, sc, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # a power of two moves every group exponent and nothing else
+    c = run((X * np.float32(2.0 ** -37)).astype(np.float32), qw, sc, dev)
+    assert np.array_equal(c, (a * np.float32(2.0 ** -37)).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 45, 96), (2, 61, 2080), (2, 4093, 7168)])
+def test_no_write_outside_y(dev, M, N, K):
+    X, W = workloads.random_case(M, N, K, seed=4)
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    run(X, qw, sc, dev, Y)
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    check(Y.cpu().numpy(), X, qw, sc, f"guarded M={M} N={N} K={K}")
+
+
+def test_non_finite_activation_propagates(dev):
+    # an infinite activation poisons its row (inf * w, or inf * 0 = NaN); the
+    # other row is unaffected
+    N, K = 96, 2048
+    X, W = workloads.random_case(2, N, K, seed=9)
+    qw, sc = oracle.quantize(W)
+    X[0, 1000] = np.float32(np.inf)
+    Y = run(X, qw, sc, dev)
+    assert not np.any(np.isfinite(Y[0]))
+    check(Y[1:], X[1:], qw, sc, "finite row next to an infinite one")

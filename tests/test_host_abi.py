@@ -38,6 +38,17 @@ def test_status_strings(lib):
     assert binding.w4a16_status_str(99) == "unknown status"
 
 
+def test_gemv_kernel(lib):
+    # matrix-core decode GEMV for M <= 2 and K <= 8192, the fp32 FMA kernels otherwise
+    assert binding.w4a16_gemv_kernel(1, 4096, 7168) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(2, 7, 8192) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(3, 64, 256) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(0, 64, 256) == 0
+    assert binding.w4a16_gemv_kernel(1, 64, 250) == 0
+    assert binding.w4a16_gemv_kernel(1, 0, 256) == 0
+
+
 def test_select_path(lib):
     assert binding.w4a16_select_path(1, 4096, 7168) == binding.W4A16_PATH_GEMV
     assert binding.w4a16_select_path(4, 4096, 7168) == binding.W4A16_PATH_GEMV
