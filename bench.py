@@ -58,7 +58,7 @@ LIMB_PATHS = ("split", "packed", "decode-packed", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
-                "swiglu": ["gemv.hip", "gemv_common.h"],
+                "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "decode-packed": ["packed_gemv.hip", "gemv_common.h", "limbs.h"],
@@ -325,7 +325,8 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
     # the limb paths issue fp16 matrix instructions (so does the GEMV path's
     # matrix-core kernel): their compute roof is the fp16 peak
     split = path in LIMB_PATHS or (
-        resolved == "gemv" and pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == pkg.W4A16_GEMV_MFMA)
+        resolved in ("gemv", "swiglu")
+        and pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == pkg.W4A16_GEMV_MFMA)
     peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
     if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

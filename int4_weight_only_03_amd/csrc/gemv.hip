@@ -57,7 +57,6 @@ __device__ __forceinline__ long w_row(long rowbase, int slot, int i, int S, long
   return (kSw && i >= RBL) ? nl + N / 2 : nl;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Fast kernel (M = MT).  Thread t < kLoaders stages the MT rows of X in LDS;
 // thread kLoaders + s*G + c (c < G, s < S) is compute thread (slot s, group
@@ -432,6 +431,8 @@ hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scal
 
 hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const float *scales,
                               float *Y, int M, int F, int K, hipStream_t stream) {
+  if (gemv_mfma_supported(M, K))  // matrix-core decode GEMV (gemv_mfma.hip)
+    return launch_gemv_mfma_swiglu(X, qweight, scales, Y, M, F, K, stream);
   return launch<true>(X, qweight, scales, Y, M, 2 * F, K, stream);
 }
 

@@ -20,6 +20,9 @@ __device__ __forceinline__ uint4 load_stream16(const uint4 *p) {
 
 __device__ __forceinline__ float load_stream4(const float *p) { return __builtin_nontemporal_load(p); }
 
+// SwiGLU epilogue of the fused gate/up GEMV: silu(g) * u, silu(g) = g / (1 + exp(-g))
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // sum over the group of x_k * 16*(q_k - 8): the 16*(q-8) are exact signed
 // bytes, each met by one fp32 FMA (one rounding per term).
 __device__ __forceinline__ float group_dot16(const float (&x)[32], uint4 w) {

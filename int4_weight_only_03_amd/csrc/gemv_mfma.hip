@@ -30,6 +30,11 @@
 //    across the wave's rows by permlane swaps, across waves in LDS in wave
 //    order.  No atomics: every output is summed in a fixed order.
 //
+// Fused gate/up SwiGLU (kSw): W holds 2F rows, gate rows 0..F-1 then up rows
+// F..2F-1.  A workgroup's 4R outputs n need gate row n and up row F + n, so a
+// lane carries 2R row quads (gate quads, then up quads); the writer stores
+// silu(gate) * up and neither product reaches memory.
+//
 // Loads: each lane first loads its 8 activations (the group's quarter j) and
 // then all of its weight and scale loads, so the weights stream while the
 // activations are split.  One workgroup covers 4R rows and all groups (one
@@ -68,11 +73,14 @@ __device__ __forceinline__ void split_block_wide(const float4 a, const float4 c,
 // its [MT][4R] partial sums.
 constexpr size_t mx_wave_lds(int MT) { return size_t(16) * 2 * MT * 64; }
 static_assert(mx_wave_lds(1) >= 1 * 4 * 8 * sizeof(float), "partials fit the limb region");
+// (at most 8 row quads per lane: R <= 8 plain, R <= 4 with kSw)
 
-template <int MT, int R>
+// N: outputs per row of Y (F for kSw, whose W has 2N rows)
+template <int MT, int R, bool kSw>
 __global__ void __launch_bounds__(1024)
 gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
         float *__restrict__ Y, int M, int N, int G) {
+  constexpr int RL = kSw ? 2 * R : R;  // row quads per lane (gate quads, then up quads)
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -92,18 +100,19 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
     xa[m][0] = xp[0];
     xa[m][1] = xp[1];
   }
-  uint4 w[R];
-  float s[R];
+  uint4 w[RL];
+  float s[RL];
   {
-    // block-relative 32-bit offsets; rows past N read the last row
+    // block-relative 32-bit offsets; rows past N read the last row (of their half)
     const uint4 *qb = qw + rowbase * G;
     const float *sb = sc + rowbase * G;
     const int nmax = int(std::min(long(N) - 1 - rowbase, long(4 * R - 1)));
+    const long up = long(N) * G;  // kSw: the up half starts N rows further
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const int off = std::min(4 * q + j, nmax) * G + gc;
-      w[q] = load_stream16(qb + off);
-      s[q] = load_stream4(sb + off);
+    for (int q = 0; q < RL; ++q) {
+      const int off = std::min(4 * (q % R) + j, nmax) * G + gc;
+      w[q] = load_stream16(qb + off + (q >= R ? up : 0));
+      s[q] = load_stream4(sb + off + (q >= R ? up : 0));
     }
   }
 
@@ -138,9 +147,9 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
     else a[c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  float acc[MT][R];
+  float acc[MT][RL];
 #pragma unroll
-  for (int q = 0; q < R; ++q) {
+  for (int q = 0; q < RL; ++q) {
     const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
     floatx4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -165,7 +174,7 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
+    for (int q = 0; q < RL; ++q) {
       float v = acc[m][q];
       v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
       v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
@@ -173,37 +182,43 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
       v = __uint_as_float(h32[0]) + __uint_as_float(h32[1]);
       const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
       v = __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
-      if (lane < 4) red[m * (4 * R) + 4 * q + lane] = v;
+      if (lane < 4) red[m * (4 * RL) + 4 * q + lane] = v;
     }
   __syncthreads();
   for (int o = threadIdx.x; o < MT * 4 * R; o += blockDim.x) {
     const int m = o / (4 * R), r = o - m * (4 * R);
-    float v = 0.0f;
-    for (int ww = 0; ww < int(blockDim.x >> 6); ++ww)
-      v += reinterpret_cast<const float *>(smem + ww * mx_wave_lds(MT))[m * (4 * R) + r];
+    float v = 0.0f, u = 0.0f;
+    for (int ww = 0; ww < int(blockDim.x >> 6); ++ww) {
+      const float *p = reinterpret_cast<const float *>(smem + ww * mx_wave_lds(MT)) + m * (4 * RL);
+      v += p[r];
+      if (kSw) u += p[4 * R + r];
+    }
     const long n = rowbase + r;
-    if (m < M && n < N) Y[long(m) * N + n] = v;
+    if (m < M && n < N) Y[long(m) * N + n] = kSw ? silu_mul(v, u) : v;
   }
 }
 
-template <int MT, int R>
+template <int MT, int R, bool kSw>
 hipError_t run_mx(const float *X, const int32_t *qw, const float *sc, float *Y, int M, int N,
                   int G, hipStream_t stream) {
   const int waves = (G + 15) / 16;
   const int blocks = int((long(N) + 4 * R - 1) / (4 * R));
-  hipLaunchKernelGGL((gemv_mx<MT, R>), dim3(blocks), dim3(waves * 64), waves * mx_wave_lds(MT),
-                     stream, X, reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G);
+  hipLaunchKernelGGL((gemv_mx<MT, R, kSw>), dim3(blocks), dim3(waves * 64),
+                     waves * mx_wave_lds(MT), stream, X, reinterpret_cast<const uint4 *>(qw), sc,
+                     Y, M, N, G);
   return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool kSw>
 hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc, float *Y, int M,
                        int N, int G, hipStream_t stream) {
   switch (R) {
-    case 8: return run_mx<MT, 8>(X, qw, sc, Y, M, N, G, stream);
-    case 4: return run_mx<MT, 4>(X, qw, sc, Y, M, N, G, stream);
-    case 2: return run_mx<MT, 2>(X, qw, sc, Y, M, N, G, stream);
-    default: return run_mx<MT, 1>(X, qw, sc, Y, M, N, G, stream);
+    case 8:
+      if constexpr (!kSw) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
+      return hipErrorInvalidValue;
+    case 4: return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
+    case 2: return run_mx<MT, 2, kSw>(X, qw, sc, Y, M, N, G, stream);
+    default: return run_mx<MT, 1, kSw>(X, qw, sc, Y, M, N, G, stream);
   }
 }
 
@@ -230,8 +245,17 @@ hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float 
   if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
   const int G = K / kGroup;
   const int R = gemv_mfma_quads(N);
-  return M == 1 ? dispatch_mx<1>(R, X, qweight, scales, Y, M, N, G, stream)
-                : dispatch_mx<2>(R, X, qweight, scales, Y, M, N, G, stream);
+  return M == 1 ? dispatch_mx<1, false>(R, X, qweight, scales, Y, M, N, G, stream)
+                : dispatch_mx<2, false>(R, X, qweight, scales, Y, M, N, G, stream);
+}
+
+hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const float *scales,
+                                   float *Y, int M, int F, int K, hipStream_t stream) {
+  if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  const int R = std::min(gemv_mfma_quads(F), 4);  // each lane carries gate and up quads
+  return M == 1 ? dispatch_mx<1, true>(R, X, qweight, scales, Y, M, F, G, stream)
+                : dispatch_mx<2, true>(R, X, qweight, scales, Y, M, F, G, stream);
 }
 
 }  // namespace w4a16

@@ -22,6 +22,9 @@ bool gemv_mfma_supported(int M, int K);
 int gemv_mfma_quads(int N);
 hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float *scales, float *Y,
                             int M, int N, int K, hipStream_t stream);
+// the same with the fused gate/up SwiGLU epilogue (W: 2F rows, gate then up; Y[M][F])
+hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const float *scales,
+                                   float *Y, int M, int F, int K, hipStream_t stream);
 
 // Tiled path: fp32 MFMA (32x32x2) on weight tiles dequantized into registers.
 hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
