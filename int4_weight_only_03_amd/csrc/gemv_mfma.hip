@@ -53,18 +53,18 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMxMaxGroups = 256;  // 16 waves of 16 groups: K <= 8192
 
-// Limbs of 8 prescaled activations a = x[k..k+3], c = x[k+4..k+7] in the
-// order the nibble conversion produces (x0 x4 x1 x5 x2 x6 x3 x7):
-// hi = f16(x * 2^e), lo = f16((x * 2^e - hi) * 2^11).
+// Limbs of 8 activations a = x[k..k+3], c = x[k+4..k+7] in the order the
+// nibble conversion produces (x0 x4 x1 x5 x2 x6 x3 x7):
+// hi = f16(x * 2^e), lo = f16(x * 2^(e+11) - 2^11 * hi)  (= f16((x * 2^e - hi) * 2^11);
+// both products by powers of two and the difference are exact in fp32).
 __device__ __forceinline__ void split_block_wide(const float4 a, const float4 c, int e, half8_t &h,
                                                  half8_t &l) {
   const float v[8] = {a.x, c.x, a.y, c.y, a.z, c.z, a.w, c.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float xs = ldexpf(v[i], e);
-    const _Float16 hv = (_Float16)xs;
+    const _Float16 hv = (_Float16)ldexpf(v[i], e);
     h[i] = hv;
-    l[i] = (_Float16)((xs - (float)hv) * 2048.0f);  // xs - hv is exact; * 2^11 exact
+    l[i] = (_Float16)__builtin_fmaf((float)hv, -2048.0f, ldexpf(v[i], e + 11));
   }
 }
 
@@ -123,11 +123,16 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   for (int m = 0; m < MT; ++m) {
     if (!gv) xa[m][0] = xa[m][1] = make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 a0 = xa[m][0], a1 = xa[m][1];
-    float mx = fmaxf(fmaxf(fmaxf(fabsf(a0.x), fabsf(a0.y)), fmaxf(fabsf(a0.z), fabsf(a0.w))),
-                     fmaxf(fmaxf(fabsf(a1.x), fabsf(a1.y)), fmaxf(fabsf(a1.z), fabsf(a1.w))));
+    // maximum magnitude as an unsigned compare of the sign-cleared bits (same
+    // order as the magnitudes; a NaN compares above every finite value)
+    uint32_t mb = std::max(std::max(std::max(__float_as_uint(a0.x) & 0x7fffffffu, __float_as_uint(a0.y) & 0x7fffffffu),
+                                    std::max(__float_as_uint(a0.z) & 0x7fffffffu, __float_as_uint(a0.w) & 0x7fffffffu)),
+                           std::max(std::max(__float_as_uint(a1.x) & 0x7fffffffu, __float_as_uint(a1.y) & 0x7fffffffu),
+                                    std::max(__float_as_uint(a1.z) & 0x7fffffffu, __float_as_uint(a1.w) & 0x7fffffffu)));
     // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad gets the group maximum
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xf, 0xf, false)));
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xf, 0xf, false)));
+    mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0xB1, 0xf, 0xf, false)));
+    mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0x4E, 0xf, 0xf, false)));
+    const float mx = __uint_as_float(mb);
     // e in [-113, 126]: 2^-e is a normal fp32 number.  Groups below 2^-112
     // keep fewer limb bits; their absolute error stays below 2^-130.
     const int e = std::min(row_exponent(mx), 126);
@@ -140,12 +145,11 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   // the wave reads back what its own lanes wrote (LDS operations of one wave
   // complete in order)
   __builtin_amdgcn_wave_barrier();
-  half8_t a[4];  // A operand: limb row j (MT = 1: rows 2, 3 are zero)
+  // A operand: limb row j.  With MT = 1, rows 2 and 3 repeat rows 0 and 1;
+  // the products of a row depend only on that row, and D rows 2, 3 are unused.
+  half8_t a[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (j < 2 * MT) a[c] = lb[(b * 2 * MT + j) * 4 + c];
-    else a[c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int c = 0; c < 4; ++c) a[c] = lb[(b * 2 * MT + (j & (2 * MT - 1))) * 4 + c];
 
   float acc[MT][RL];
 #pragma unroll
