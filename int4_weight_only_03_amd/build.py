@@ -60,21 +60,27 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libw4a16.so; returns the library path."""
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel) and link libw4a16.so; returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     cc = hipcc()
     os.makedirs(OBJ, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in HOST_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, "-ffp-contract=off", "-fno-fast-math", "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
+        cmds.append([cc, *COMMON, "-ffp-contract=off", "-fno-fast-math", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in DEVICE_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o",
-              obj], verbose)
+        cmds.append([cc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
+    jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()  # re-raises the first failed compile
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
