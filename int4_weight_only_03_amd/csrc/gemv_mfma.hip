@@ -1,4 +1,4 @@
-// Decode GEMV (M <= 2) on the 4x4x4 fp16 matrix instructions.
+// Decode GEMV (M <= 4) on the 4x4x4 fp16 matrix instructions.
 //
 // The decode path exists for memory-bound MoE inference and aims at the HBM
 // bandwidth peak ("The Quiet Commit: How a Single Plan Update Closed Phase 3
@@ -20,7 +20,8 @@
 //    fp16 weight code (q - 8) are exact in fp32.
 //  * v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products.  Block b
 //    of a wave is group g = 16*wave + b.  Its A operand (4 x 4) holds the limb
-//    rows (hi and lo of each activation row), its B operand (4 x 4) four W
+//    rows (hi and lo of two activation rows; M = 3, 4 take a second A operand
+//    against the same converted weights), its B operand (4 x 4) four W
 //    rows; eight instructions cover the group's 32 k, accumulating from zero.
 //    Lane 4b + j is W row j as B operand and receives D[.][j] (the limb sums
 //    of that row), so the lane that loaded a row's 16 bytes and scale also
@@ -68,35 +69,35 @@ __device__ __forceinline__ void split_block_wide(const float4 a, const float4 c,
   }
 }
 
-// LDS: per wave [16 groups][2*MT limb rows][4 quarters] of 8 fp16 (at most
-// 64 KB).  Once a wave has read its limbs back, the start of its region holds
-// its [MT][4R] partial sums.
+// LDS: per wave [16 groups][2*MT limb rows][4 quarters] of 8 fp16 (2 KB per
+// activation row, at most 128 KB).  Once a wave has read its limbs back, the
+// start of its region holds its [MT][4*RL] partial sums.
 constexpr size_t mx_wave_lds(int MT) { return size_t(16) * 2 * MT * 64; }
 static_assert(mx_wave_lds(1) >= 1 * 4 * 8 * sizeof(float), "partials fit the limb region");
 // (at most 8 row quads per lane: R <= 8 plain, R <= 4 with kSw)
 
-// N: outputs per row of Y (F for kSw, whose W has 2N rows)
+// One workgroup: rows rowbase .. rowbase + 4R - 1 of the N x K matrix at
+// qw/sc (kSw: gate rows there, up rows N further) against MT activation rows
+// xr[m] (rows past the real ones point at a real row and feed only results
+// that are not stored), results to yr[m][n] for yr[m] != nullptr and n < N.
 template <int MT, int R, bool kSw>
-__global__ void __launch_bounds__(1024)
-gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
-        float *__restrict__ Y, int M, int N, int G) {
+__device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint4 *__restrict__ qw,
+                                        const float *__restrict__ sc, float *const (&yr)[MT],
+                                        int N, int G, long rowbase, unsigned char *smem) {
   constexpr int RL = kSw ? 2 * R : R;  // row quads per lane (gate quads, then up quads)
-  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int MS = (MT + 1) / 2;     // A operands of 4 limb rows (2 activation rows each)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = lane >> 2, j = lane & 3;
   const int g = wave * 16 + b;
   const bool gv = g < G;
   const int gc = gv ? g : G - 1;  // clamped: every load stays in bounds
-  const long K = long(G) * kGroup;
-  const long rowbase = long(blockIdx.x) * (4 * R);
 
-  // activations first (quarter j of group gc for each row), then the weights
+  // activations first (quarter j of group gc of each row), then the weights
   float4 xa[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int mr = m < M ? m : 0;
-    const float4 *xp = reinterpret_cast<const float4 *>(X + mr * K + long(gc) * kGroup + 8 * j);
+    const float4 *xp = reinterpret_cast<const float4 *>(xr[m] + long(gc) * kGroup + 8 * j);
     xa[m][0] = xp[0];
     xa[m][1] = xp[1];
   }
@@ -145,31 +146,43 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   // the wave reads back what its own lanes wrote (LDS operations of one wave
   // complete in order)
   __builtin_amdgcn_wave_barrier();
-  // A operand: limb row j.  With MT = 1, rows 2 and 3 repeat rows 0 and 1;
-  // the products of a row depend only on that row, and D rows 2, 3 are unused.
-  half8_t a[4];
+  // A operand p: limb rows 4p .. 4p+3 (activation rows 2p, 2p+1).  With MT = 1,
+  // rows 2 and 3 repeat rows 0 and 1; the products of a row depend only on
+  // that row, and those D rows are unused.
+  half8_t a[MS][4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) a[c] = lb[(b * 2 * MT + (j & (2 * MT - 1))) * 4 + c];
+  for (int p = 0; p < MS; ++p)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      a[p][c] = lb[(b * 2 * MT + (MT == 1 ? (j & 1) : 4 * p + j)) * 4 + c];
 
   float acc[MT][RL];
 #pragma unroll
   for (int q = 0; q < RL; ++q) {
     const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-    floatx4 d = {0.f, 0.f, 0.f, 0.f};
+    half8_t bw[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {  // word c: k = 8c..8c+7 in the order of split_block
-      const half8_t bw = nibbles_to_f16(u[c]);
-      const half4_t a0 = {a[c][0], a[c][1], a[c][2], a[c][3]};
-      const half4_t a1 = {a[c][4], a[c][5], a[c][6], a[c][7]};
-      const half4_t b0 = {bw[0], bw[1], bw[2], bw[3]};
-      const half4_t b1 = {bw[4], bw[5], bw[6], bw[7]};
-      d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c) bw[c] = nibbles_to_f16(u[c]);  // k = 8c..8c+7, split_block order
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float sp = gv ? s[q] * inv[m] : 0.0f;  // exact: a power-of-two factor
-      acc[m][q] = sp * fmaf(d[2 * m + 1], 0x1p-11f, d[2 * m]);
+    for (int p = 0; p < MS; ++p) {
+      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const half4_t a0 = {a[p][c][0], a[p][c][1], a[p][c][2], a[p][c][3]};
+        const half4_t a1 = {a[p][c][4], a[p][c][5], a[p][c][6], a[p][c][7]};
+        const half4_t b0 = {bw[c][0], bw[c][1], bw[c][2], bw[c][3]};
+        const half4_t b1 = {bw[c][4], bw[c][5], bw[c][6], bw[c][7]};
+        d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = 2 * p + h;
+        if (m < MT) {
+          const float sp = gv ? s[q] * inv[m] : 0.0f;  // exact: a power-of-two factor
+          acc[m][q] = sp * fmaf(d[2 * h + 1], 0x1p-11f, d[2 * h]);
+        }
+      }
     }
   }
 
@@ -198,8 +211,26 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
       if (kSw) u += p[4 * R + r];
     }
     const long n = rowbase + r;
-    if (m < M && n < N) Y[long(m) * N + n] = kSw ? silu_mul(v, u) : v;
+    if (yr[m] != nullptr && n < N) yr[m][n] = kSw ? silu_mul(v, u) : v;
   }
+}
+
+// N: outputs per row of Y (F for kSw, whose W has 2N rows).  MT = 4 serves
+// M = 3 and 4.
+template <int MT, int R, bool kSw>
+__global__ void __launch_bounds__(1024)
+gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
+        float *__restrict__ Y, int M, int N, int G) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const long K = long(G) * kGroup;
+  const float *xr[MT];
+  float *yr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    xr[m] = X + (m < M ? m : 0) * K;
+    yr[m] = m < M ? Y + long(m) * N : nullptr;
+  }
+  mx_pass<MT, R, kSw>(xr, qw, sc, yr, N, G, long(blockIdx.x) * (4 * R), smem);
 }
 
 template <int MT, int R, bool kSw>
@@ -217,9 +248,9 @@ template <int MT, bool kSw>
 hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc, float *Y, int M,
                        int N, int G, hipStream_t stream) {
   switch (R) {
-    case 8:
-      if constexpr (!kSw) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
-      return hipErrorInvalidValue;
+    case 8:  // 8 row quads: plain GEMV with up to 2 rows (more would spill)
+      if constexpr (!kSw && MT <= 2) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
+      else return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
     case 4: return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
     case 2: return run_mx<MT, 2, kSw>(X, qw, sc, Y, M, N, G, stream);
     default: return run_mx<MT, 1, kSw>(X, qw, sc, Y, M, N, G, stream);
@@ -229,7 +260,7 @@ hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc
 }  // namespace
 
 bool gemv_mfma_supported(int M, int K) {
-  return M >= 1 && M <= 2 && K / kGroup <= kMxMaxGroups;
+  return M >= 1 && M <= 4 && K / kGroup <= kMxMaxGroups;
 }
 
 // Quads of rows per lane: the most that still leaves at least 224 workgroups
@@ -249,8 +280,11 @@ hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float 
   if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
   const int G = K / kGroup;
   const int R = gemv_mfma_quads(N);
-  return M == 1 ? dispatch_mx<1, false>(R, X, qweight, scales, Y, M, N, G, stream)
-                : dispatch_mx<2, false>(R, X, qweight, scales, Y, M, N, G, stream);
+  switch (M) {
+    case 1: return dispatch_mx<1, false>(R, X, qweight, scales, Y, M, N, G, stream);
+    case 2: return dispatch_mx<2, false>(R, X, qweight, scales, Y, M, N, G, stream);
+    default: return dispatch_mx<4, false>(R, X, qweight, scales, Y, M, N, G, stream);
+  }
 }
 
 hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const float *scales,
@@ -258,8 +292,11 @@ hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const
   if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
   const int G = K / kGroup;
   const int R = std::min(gemv_mfma_quads(F), 4);  // each lane carries gate and up quads
-  return M == 1 ? dispatch_mx<1, true>(R, X, qweight, scales, Y, M, F, G, stream)
-                : dispatch_mx<2, true>(R, X, qweight, scales, Y, M, F, G, stream);
+  switch (M) {
+    case 1: return dispatch_mx<1, true>(R, X, qweight, scales, Y, M, F, G, stream);
+    case 2: return dispatch_mx<2, true>(R, X, qweight, scales, Y, M, F, G, stream);
+    default: return dispatch_mx<4, true>(R, X, qweight, scales, Y, M, F, G, stream);
+  }
 }
 
 }  // namespace w4a16
