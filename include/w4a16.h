@@ -64,7 +64,7 @@ extern "C" {
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
-#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV; for M <= 4 and
+#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV; for M <= 8 and
                                  K <= 8192 on the 4x4x4 fp16 matrix instructions
                                  (w4a16_gemv_kernel) */
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
@@ -119,7 +119,7 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
  *     silu(g) = g / (1 + exp(-g)),
  * with g and u the same fp32 group-scaled sums as w4a16_gemm and the epilogue
  * in fp32.  Y is [M][F] (not 2F); the gate/up outputs never reach memory.
- * Runs on the GEMV kernels (the matrix-core one for M <= 4 and K <= 8192,
+ * Runs on the GEMV kernels (the matrix-core one for M <= 8 and K <= 8192,
  * w4a16_gemv_kernel; any M accepted).  Errors as
  * w4a16_gemm with N = 2F.
  */
@@ -260,7 +260,7 @@ size_t w4a16_small_packed_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
 
 /* Kernels behind W4A16_PATH_GEMV. */
-#define W4A16_GEMV_MFMA 1     /* M <= 4, K <= 8192: v_mfma_f32_4x4x4_16b_f16 on exact weight
+#define W4A16_GEMV_MFMA 1     /* M <= 8, K <= 8192: v_mfma_f32_4x4x4_16b_f16 on exact weight
                                  codes (nibble - 8) and two fp16 limbs of each activation; every
                                  group of 32 activations is scaled by a power of two (max |x|
                                  into [2^14, 2^15)) before the split, so the limbs hold 22
@@ -275,7 +275,9 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
  * Knowledge".) */
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
 
-/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE). */
+/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE): the GEMV
+ * path for M <= 4, and for M <= 8 when it runs the matrix-core kernel
+ * (K <= 8192); the tiled path otherwise. */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 
 /*

@@ -1,4 +1,4 @@
-// Decode GEMV (M <= 4) on the 4x4x4 fp16 matrix instructions.
+// Decode GEMV (M <= 8) on the 4x4x4 fp16 matrix instructions.
 //
 // The decode path exists for memory-bound MoE inference and aims at the HBM
 // bandwidth peak ("The Quiet Commit: How a Single Plan Update Closed Phase 3
@@ -20,8 +20,8 @@
 //    fp16 weight code (q - 8) are exact in fp32.
 //  * v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products.  Block b
 //    of a wave is group g = 16*wave + b.  Its A operand (4 x 4) holds the limb
-//    rows (hi and lo of two activation rows; M = 3, 4 take a second A operand
-//    against the same converted weights), its B operand (4 x 4) four W
+//    rows (hi and lo of two activation rows; M = 3..8 take up to four A
+//    operands against the same converted weights), its B operand (4 x 4) four W
 //    rows; eight instructions cover the group's 32 k, accumulating from zero.
 //    Lane 4b + j is W row j as B operand and receives D[.][j] (the limb sums
 //    of that row), so the lane that loaded a row's 16 bytes and scale also
@@ -69,12 +69,15 @@ __device__ __forceinline__ void split_block_wide(const float4 a, const float4 c,
   }
 }
 
-// LDS: per wave [16 groups][2*MT limb rows][4 quarters] of 8 fp16 (2 KB per
-// activation row, at most 128 KB).  Once a wave has read its limbs back, the
-// start of its region holds its [MT][4*RL] partial sums.
-constexpr size_t mx_wave_lds(int MT) { return size_t(16) * 2 * MT * 64; }
+// LDS: per wave [16 groups][limb rows of one A operand][4 quarters] of 8 fp16:
+// 2 limb rows for MT = 1 (2 KB), 4 otherwise (4 KB); with MT > 2 the A
+// operands pass through it one after the other.  Once a wave has read its
+// limbs back, the start of its region holds its [MT][4*RL] partial sums.
+constexpr int mx_limb_rows(int MT) { return MT == 1 ? 2 : 4; }
+constexpr size_t mx_wave_lds(int MT) { return size_t(16) * mx_limb_rows(MT) * 64; }
 static_assert(mx_wave_lds(1) >= 1 * 4 * 8 * sizeof(float), "partials fit the limb region");
-// (at most 8 row quads per lane: R <= 8 plain, R <= 4 with kSw)
+static_assert(mx_wave_lds(8) >= 8 * 4 * 4 * sizeof(float), "partials fit the limb region");
+// (row quads per lane: at most 8 for MT <= 2, 4 for MT = 4, 2 for MT = 8)
 
 // One workgroup: rows rowbase .. rowbase + 4R - 1 of the N x K matrix at
 // qw/sc (kSw: gate rows there, up rows N further) against MT activation rows
@@ -117,44 +120,48 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
     }
   }
 
-  // group maxima (the 4 lanes of a quad hold one group), exponents, limbs
+  // group maxima (the 4 lanes of a quad hold one group), exponents, limbs;
+  // A operand p holds limb rows 4p .. 4p+3 (activation rows 2p, 2p+1), staged
+  // through the wave's own LDS region (LDS operations of one wave complete in
+  // order, so each read sees the writes before it and precedes the writes
+  // after it).  With MT = 1, rows 2 and 3 repeat rows 0 and 1; the products of
+  // a row depend only on that row, and those D rows are unused.
+  constexpr int LR = mx_limb_rows(MT);
   half8_t *lb = reinterpret_cast<half8_t *>(smem + wave * mx_wave_lds(MT));
   float inv[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (!gv) xa[m][0] = xa[m][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 a0 = xa[m][0], a1 = xa[m][1];
-    // maximum magnitude as an unsigned compare of the sign-cleared bits (same
-    // order as the magnitudes; a NaN compares above every finite value)
-    uint32_t mb = std::max(std::max(std::max(__float_as_uint(a0.x) & 0x7fffffffu, __float_as_uint(a0.y) & 0x7fffffffu),
-                                    std::max(__float_as_uint(a0.z) & 0x7fffffffu, __float_as_uint(a0.w) & 0x7fffffffu)),
-                           std::max(std::max(__float_as_uint(a1.x) & 0x7fffffffu, __float_as_uint(a1.y) & 0x7fffffffu),
-                                    std::max(__float_as_uint(a1.z) & 0x7fffffffu, __float_as_uint(a1.w) & 0x7fffffffu)));
-    // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad gets the group maximum
-    mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0xB1, 0xf, 0xf, false)));
-    mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0x4E, 0xf, 0xf, false)));
-    const float mx = __uint_as_float(mb);
-    // e in [-113, 126]: 2^-e is a normal fp32 number.  Groups below 2^-112
-    // keep fewer limb bits; their absolute error stays below 2^-130.
-    const int e = std::min(row_exponent(mx), 126);
-    inv[m] = __int_as_float((127 - e) << 23);
-    half8_t h, l;
-    split_block_wide(a0, a1, e, h, l);
-    lb[(b * 2 * MT + 2 * m) * 4 + j] = h;
-    lb[(b * 2 * MT + 2 * m + 1) * 4 + j] = l;
-  }
-  // the wave reads back what its own lanes wrote (LDS operations of one wave
-  // complete in order)
-  __builtin_amdgcn_wave_barrier();
-  // A operand p: limb rows 4p .. 4p+3 (activation rows 2p, 2p+1).  With MT = 1,
-  // rows 2 and 3 repeat rows 0 and 1; the products of a row depend only on
-  // that row, and those D rows are unused.
   half8_t a[MS][4];
 #pragma unroll
-  for (int p = 0; p < MS; ++p)
+  for (int p = 0; p < MS; ++p) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      a[p][c] = lb[(b * 2 * MT + (MT == 1 ? (j & 1) : 4 * p + j)) * 4 + c];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int m = 2 * p + hh;
+      if (m >= MT) break;
+      if (!gv) xa[m][0] = xa[m][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 a0 = xa[m][0], a1 = xa[m][1];
+      // maximum magnitude as an unsigned compare of the sign-cleared bits (same
+      // order as the magnitudes; a NaN compares above every finite value)
+      uint32_t mb = std::max(std::max(std::max(__float_as_uint(a0.x) & 0x7fffffffu, __float_as_uint(a0.y) & 0x7fffffffu),
+                                      std::max(__float_as_uint(a0.z) & 0x7fffffffu, __float_as_uint(a0.w) & 0x7fffffffu)),
+                             std::max(std::max(__float_as_uint(a1.x) & 0x7fffffffu, __float_as_uint(a1.y) & 0x7fffffffu),
+                                      std::max(__float_as_uint(a1.z) & 0x7fffffffu, __float_as_uint(a1.w) & 0x7fffffffu)));
+      // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad gets the group maximum
+      mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0xB1, 0xf, 0xf, false)));
+      mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0x4E, 0xf, 0xf, false)));
+      const float mx = __uint_as_float(mb);
+      // e in [-113, 126]: 2^-e is a normal fp32 number.  Groups below 2^-112
+      // keep fewer limb bits; their absolute error stays below 2^-130.
+      const int e = std::min(row_exponent(mx), 126);
+      inv[m] = __int_as_float((127 - e) << 23);
+      half8_t h, l;
+      split_block_wide(a0, a1, e, h, l);
+      lb[(b * LR + 2 * hh) * 4 + j] = h;
+      lb[(b * LR + 2 * hh + 1) * 4 + j] = l;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[p][c] = lb[(b * LR + (MT == 1 ? (j & 1) : j)) * 4 + c];
+    __builtin_amdgcn_wave_barrier();
+  }
 
   float acc[MT][RL];
 #pragma unroll
@@ -216,7 +223,7 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
 }
 
 // N: outputs per row of Y (F for kSw, whose W has 2N rows).  MT = 4 serves
-// M = 3 and 4.
+// M = 3 and 4, MT = 8 serves M = 5 .. 8.
 template <int MT, int R, bool kSw>
 __global__ void __launch_bounds__(1024)
 gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
@@ -247,12 +254,20 @@ hipError_t run_mx(const float *X, const int32_t *qw, const float *sc, float *Y, 
 template <int MT, bool kSw>
 hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc, float *Y, int M,
                        int N, int G, hipStream_t stream) {
+  // row quads per lane are capped so that no variant spills: 8 only for the
+  // plain GEMV of up to 2 rows, 2 (1 with kSw) for 8 rows
+  constexpr int kCap = MT <= 2 ? (kSw ? 4 : 8) : (MT == 4 ? 4 : (kSw ? 1 : 2));
+  R = std::min(R, kCap);
   switch (R) {
-    case 8:  // 8 row quads: plain GEMV with up to 2 rows (more would spill)
-      if constexpr (!kSw && MT <= 2) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
-      else return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
-    case 4: return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
-    case 2: return run_mx<MT, 2, kSw>(X, qw, sc, Y, M, N, G, stream);
+    case 8:
+      if constexpr (kCap >= 8) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
+      else return hipErrorInvalidValue;
+    case 4:
+      if constexpr (kCap >= 4) return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
+      else return hipErrorInvalidValue;
+    case 2:
+      if constexpr (kCap >= 2) return run_mx<MT, 2, kSw>(X, qw, sc, Y, M, N, G, stream);
+      else return hipErrorInvalidValue;
     default: return run_mx<MT, 1, kSw>(X, qw, sc, Y, M, N, G, stream);
   }
 }
@@ -260,7 +275,7 @@ hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc
 }  // namespace
 
 bool gemv_mfma_supported(int M, int K) {
-  return M >= 1 && M <= 4 && K / kGroup <= kMxMaxGroups;
+  return M >= 1 && M <= 8 && K / kGroup <= kMxMaxGroups;
 }
 
 // Quads of rows per lane: the most that still leaves at least 224 workgroups
@@ -283,7 +298,9 @@ hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float 
   switch (M) {
     case 1: return dispatch_mx<1, false>(R, X, qweight, scales, Y, M, N, G, stream);
     case 2: return dispatch_mx<2, false>(R, X, qweight, scales, Y, M, N, G, stream);
-    default: return dispatch_mx<4, false>(R, X, qweight, scales, Y, M, N, G, stream);
+    case 3:
+    case 4: return dispatch_mx<4, false>(R, X, qweight, scales, Y, M, N, G, stream);
+    default: return dispatch_mx<8, false>(R, X, qweight, scales, Y, M, N, G, stream);
   }
 }
 
@@ -295,7 +312,9 @@ hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const
   switch (M) {
     case 1: return dispatch_mx<1, true>(R, X, qweight, scales, Y, M, F, G, stream);
     case 2: return dispatch_mx<2, true>(R, X, qweight, scales, Y, M, F, G, stream);
-    default: return dispatch_mx<4, true>(R, X, qweight, scales, Y, M, F, G, stream);
+    case 3:
+    case 4: return dispatch_mx<4, true>(R, X, qweight, scales, Y, M, F, G, stream);
+    default: return dispatch_mx<8, true>(R, X, qweight, scales, Y, M, F, G, stream);
   }
 }
 

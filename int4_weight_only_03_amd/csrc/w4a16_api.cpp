@@ -45,7 +45,12 @@ int validate_gemm(const float *X, const int32_t *qweight, const float *scales, f
   return W4A16_OK;
 }
 
-int select_path(int64_t M) { return M <= w4a16::kGemvMaxM ? W4A16_PATH_GEMV : W4A16_PATH_TILE; }
+int select_path(int64_t M, int64_t K) {
+  if (M <= w4a16::kGemvMaxM) return W4A16_PATH_GEMV;
+  if (M <= w4a16::kGemvMfmaMaxM && K <= W4A16_MAX_K && w4a16::gemv_mfma_supported(int(M), int(K)))
+    return W4A16_PATH_GEMV;
+  return W4A16_PATH_TILE;
+}
 
 }  // namespace
 
@@ -68,8 +73,7 @@ const char *w4a16_status_str(int status) {
 
 int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
   (void)N;
-  (void)K;
-  return select_path(M);
+  return select_path(M, K);
 }
 
 int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
@@ -78,7 +82,7 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
     return W4A16_ERR_ARG;
   int st = validate_gemm(X, qweight, scales, Y, M, N, K, group);
   if (st != W4A16_OK || M == 0 || N == 0) return st;
-  if (path == W4A16_PATH_AUTO) path = select_path(M);
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (path == W4A16_PATH_GEMV)
                      ? w4a16::launch_gemv(X, qweight, scales, Y, int(M), int(N), int(K), s)

@@ -15,7 +15,7 @@ constexpr int kGroup = 32;
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream);
 
-// Decode GEMV (M <= 4, K <= 8192) on the 4x4x4 fp16 matrix instructions:
+// Decode GEMV (M <= 8, K <= 8192) on the 4x4x4 fp16 matrix instructions:
 // exact weight codes, two fp16 limbs of each group-prescaled activation.
 // launch_gemv runs it whenever gemv_mfma_supported(M, K).
 bool gemv_mfma_supported(int M, int K);
@@ -83,7 +83,9 @@ hipError_t launch_grouped(const float *X, const int32_t *token_index, const int3
                           const int32_t *qweight, const float *scales, float *Y, int T, int R,
                           int E, int N, int K, hipStream_t stream);
 
-// Largest M the GEMV path is chosen for by default.
+// Largest M the GEMV path is chosen for by default (the fp32 FMA GEMV); up
+// to kGemvMfmaMaxM when the matrix-core GEMV takes the shape.
 constexpr int kGemvMaxM = 4;
+constexpr int kGemvMfmaMaxM = 8;
 
 }  // namespace w4a16

@@ -1,11 +1,11 @@
-"""GPU parity of the matrix-core decode GEMV (W4A16_GEMV_MFMA: M <= 4, K <= 8192).
+"""GPU parity of the matrix-core decode GEMV (W4A16_GEMV_MFMA: M <= 8, K <= 8192).
 
 The kernel computes with exact fp16 weight codes and two fp16 limbs of each
 activation group scaled by a power of two; every output must still satisfy
 |Y - Y_ref| <= 1e-5 * sum_k |x_k w_k| + 1e-6 against the fp64 oracle.  Inputs
 are seeded synthetic draws quantized by the oracle; nothing expected comes from
 the HIP path.  The cases cover groups that do not fill a wave (K not a multiple
-of 512), ragged N at every rows-per-lane setting, one to four rows, the largest
+of 512), ragged N at every rows-per-lane setting, one to eight rows, the largest
 K the kernel takes and the first K it hands to the fp32 kernel, groups of very
 different magnitudes, integer inputs that must be exact, run-to-run
 determinism, power-of-two equivariance, writes confined to Y, and non-finite
@@ -63,7 +63,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_shapes_against_oracle(dev, M, N, K):
     say(f"gemv_mfma M={M} N={N} K={K}")
@@ -73,7 +73,7 @@ def test_shapes_against_oracle(dev, M, N, K):
     check(run(X, qw, sc, dev), X, qw, sc, f"mfma {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_first_k_past_the_kernel_uses_fp32(dev, M):
     N, K = 70, 8192 + 32
     assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_FMA
@@ -82,7 +82,7 @@ def test_first_k_past_the_kernel_uses_fp32(dev, M):
     check(run(X, qw, sc, dev), X, qw, sc, f"fp32 kernel {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3])
+@pytest.mark.parametrize("M", [1, 2, 3, 7])
 def test_group_magnitudes_far_apart(dev, M):
     # each group of X at its own power of two (2^-100 .. 2^100), some groups zero,
     # some with subnormal entries, some spanning 2^26 inside the group
@@ -101,7 +101,8 @@ def test_group_magnitudes_far_apart(dev, M):
     check(run(X, qw, sc, dev), X, qw, sc, f"far-apart groups M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 7168), (2, 77, 2080), (2, 4096, 8192), (4, 513, 7168)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 7168), (2, 77, 2080), (2, 4096, 8192), (4, 513, 7168),
+                                   (8, 300, 7168), (6, 33, 96)])
 def test_integer_inputs_exact(dev, M, N, K):
     # integer activations in [-8, 8] and one power-of-two scale: every partial
     # sum is an exact fp32 integer multiple, so any order gives the oracle's value
@@ -112,7 +113,7 @@ def test_integer_inputs_exact(dev, M, N, K):
     assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
 
 
-@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
 def test_deterministic_and_scale_equivariant(dev, M):
     X, W = workloads.random_case(M, 1000, 7168, seed=78)
     qw, sc = oracle.quantize(W)
@@ -124,7 +125,8 @@ def test_deterministic_and_scale_equivariant(dev, M):
     assert np.array_equal(c, (a * np.float32(2.0 ** -37)).astype(np.float32))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 45, 96), (2, 61, 2080), (2, 4093, 7168), (3, 70, 7168)])
+@pytest.mark.parametrize("M,N,K", [(1, 45, 96), (2, 61, 2080), (2, 4093, 7168), (3, 70, 7168),
+                                   (7, 130, 2048)])
 def test_no_write_outside_y(dev, M, N, K):
     X, W = workloads.random_case(M, N, K, seed=4)
     qw, sc = oracle.quantize(W)
@@ -137,7 +139,7 @@ def test_no_write_outside_y(dev, M, N, K):
     check(Y.cpu().numpy(), X, qw, sc, f"guarded M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,bad", [(2, 0), (4, 2)])
+@pytest.mark.parametrize("M,bad", [(2, 0), (4, 2), (8, 5)])
 def test_non_finite_activation_propagates(dev, M, bad):
     # an infinite activation poisons its row (inf * w, or inf * 0 = NaN); the
     # other rows are unaffected

@@ -39,12 +39,13 @@ def test_status_strings(lib):
 
 
 def test_gemv_kernel(lib):
-    # matrix-core decode GEMV for M <= 4 and K <= 8192, the fp32 FMA kernels otherwise
+    # matrix-core decode GEMV for M <= 8 and K <= 8192, the fp32 FMA kernels otherwise
     assert binding.w4a16_gemv_kernel(1, 4096, 7168) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(2, 7, 8192) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_FMA
     assert binding.w4a16_gemv_kernel(4, 64, 256) == binding.W4A16_GEMV_MFMA
-    assert binding.w4a16_gemv_kernel(5, 64, 256) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(8, 64, 256) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(9, 64, 256) == binding.W4A16_GEMV_FMA
     assert binding.w4a16_gemv_kernel(0, 64, 256) == 0
     assert binding.w4a16_gemv_kernel(1, 64, 250) == 0
     assert binding.w4a16_gemv_kernel(1, 0, 256) == 0
@@ -53,7 +54,10 @@ def test_gemv_kernel(lib):
 def test_select_path(lib):
     assert binding.w4a16_select_path(1, 4096, 7168) == binding.W4A16_PATH_GEMV
     assert binding.w4a16_select_path(4, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(5, 4096, 7168) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(5, 4096, 7168) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(8, 4096, 7168) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(5, 4096, 8192 + 32) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(9, 4096, 7168) == binding.W4A16_PATH_TILE
     assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE
 
 
