@@ -160,37 +160,39 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int c = 0; c < 4; ++c) a[p][c] = lb[(b * LR + (MT == 1 ? (j & 1) : j)) * 4 + c];
-    __builtin_amdgcn_wave_barrier();
+    if (p + 1 < MS) __builtin_amdgcn_wave_barrier();  // the next operand's writes stay behind
   }
 
   float acc[MT][RL];
 #pragma unroll
   for (int q = 0; q < RL; ++q) {
     const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-    half8_t bw[4];
+    floatx4 d[MS];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bw[c] = nibbles_to_f16(u[c]);  // k = 8c..8c+7, split_block order
+    for (int p = 0; p < MS; ++p) d[p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < MS; ++p) {
-      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) {  // word c: k = 8c..8c+7 in the order of split_block
+      const half8_t bw = nibbles_to_f16(u[c]);
+      const half4_t b0 = {bw[0], bw[1], bw[2], bw[3]};
+      const half4_t b1 = {bw[4], bw[5], bw[6], bw[7]};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int p = 0; p < MS; ++p) {  // independent accumulators: the MFMAs interleave
         const half4_t a0 = {a[p][c][0], a[p][c][1], a[p][c][2], a[p][c][3]};
         const half4_t a1 = {a[p][c][4], a[p][c][5], a[p][c][6], a[p][c][7]};
-        const half4_t b0 = {bw[c][0], bw[c][1], bw[c][2], bw[c][3]};
-        const half4_t b1 = {bw[c][4], bw[c][5], bw[c][6], bw[c][7]};
-        d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 0, 0, 0);
+        d[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d[p], 0, 0, 0);
+        d[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d[p], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int p = 0; p < MS; ++p)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int m = 2 * p + h;
         if (m < MT) {
           const float sp = gv ? s[q] * inv[m] : 0.0f;  // exact: a power-of-two factor
-          acc[m][q] = sp * fmaf(d[2 * h + 1], 0x1p-11f, d[2 * h]);
+          acc[m][q] = sp * fmaf(d[p][2 * h + 1], 0x1p-11f, d[p][2 * h]);
         }
       }
-    }
   }
 
   // sum over the wave's groups: lanes with equal j
