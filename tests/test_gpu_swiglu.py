@@ -43,7 +43,9 @@ def run(X, qw, sc, dev, Y=None):
 
 @pytest.mark.parametrize("M,F,K", [(1, 1, 32), (1, 33, 96), (2, 70, 224), (1, 300, 256),
                                    (1, 2048, 7168), (2, 64, 2048), (3, 70, 224), (5, 128, 512),
-                                   (64, 96, 2048), (1, 129, 16384 + 32)])
+                                   (64, 96, 2048), (1, 129, 16384 + 32),
+                                   # the matrix-core GEMV with 4 and 8 activation rows
+                                   (4, 257, 7168), (8, 2048, 7168), (7, 33, 2080)])
 def test_swiglu_shapes(dev, M, F, K):
     say(f"swiglu M={M} F={F} K={K}")
     X, W = workloads.random_case(M, 2 * F, K, seed=M * 7 + F * 11 + K)
