@@ -102,6 +102,27 @@ def test_grouped_guard_band_and_determinism(dev):
     assert oracle.compare_grouped(a, X, ti, off, q, s)["ok"]
 
 
+def test_grouped_moe_decode_full_size(dev):
+    """The moe_decode workload as timed (16 tokens, top-4 of 32 experts, N=1024,
+    K=7168): every output of the public-layout and packed kernels against the
+    oracle, and the two bit for bit (the same matrix-core kernel)."""
+    X, W, ti, off = workloads.make_moe("moe_decode")
+    T, E, N, K = X.shape[0], W.shape[0], W.shape[1], W.shape[2]
+    say(f"grouped moe_decode full size T={T} E={E} N={N} K={K}, {int(np.sum(np.diff(off) == 0))} empty")
+    q, s = quantize_experts(W)
+    del W
+    Yu = run(X, ti, off, q, s, dev)
+    packed = binding.w4a16_grouped_pack(to_dev(q, dev), to_dev(s, dev))
+    Yp = binding.w4a16_gemm_grouped_packed(to_dev(X, dev), to_dev(ti, dev), to_dev(off, dev),
+                                           packed, E, N)
+    torch.cuda.synchronize()
+    Yp = Yp.cpu().numpy()
+    assert np.array_equal(Yp.view(np.uint32), Yu.view(np.uint32))
+    v = oracle.compare_grouped(Yu, X, ti, off, q, s)
+    say(f"  max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
 def test_grouped_many_experts_fallback(dev):
     # more experts than the matrix-core kernel's work list takes: the
     # LDS-staged FMA kernel runs instead
