@@ -151,3 +151,35 @@ def test_non_finite_activation_propagates(dev, M, bad):
     assert not np.any(np.isfinite(Y[bad]))
     ok = [m for m in range(M) if m != bad]
     check(Y[ok], X[ok], qw, sc, "finite rows next to an infinite one")
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 15, 16, 17, 31, 33, 64, 100, 129, 200, 255, 256]))
+        N = int(rng.integers(1, 700))
+        out.append((M, N, 32 * G))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(24, 2024))
+def test_random_shapes_against_oracle(dev, M, N, K):
+    # seeded sweep over row counts, group counts around the 16-group wave
+    # boundaries and ragged N (every rows-per-lane choice and its clamped tail)
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_MFMA
+    X, W = workloads.random_case(M, N, K, seed=M + 3 * N + 7 * K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"sweep {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,F,K", _random_shapes(12, 77))
+def test_random_swiglu_shapes_against_oracle(dev, M, F, K):
+    X, W = workloads.random_case(M, 2 * F, K, seed=M + 5 * F + 11 * K)
+    qw, sc = oracle.quantize(W)
+    Y = binding.w4a16_gemm_swiglu(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev))
+    torch.cuda.synchronize()
+    v = oracle.compare_swiglu(Y.cpu().numpy(), X, qw, sc)
+    say(f"swiglu sweep {M}x{F}x{K}: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
