@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 group-quantized GEMM on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME[,NAME]|all]
-                    [--path auto|gemv|tile|split|packed|swiglu|decode-packed|small-packed[,...]]
+                    [--path auto|gemv|tile|split|packed|swiglu|repacked|small-packed[,...]]
                     [--no-cpu]
 
 A step is one call of the chosen entry point (the whole hot path: validate,
@@ -12,9 +12,10 @@ w4a16_gemm_split (activation prep, fp16-MFMA contraction, split-K reduce) for
 split; w4a16_gemm_split_packed for packed, whose one-time weight repack runs
 before the timed region and is reported on its own (repack_ms_one_time);
 w4a16_gemm_swiglu for swiglu (the workload's W read as gate rows then up rows,
-Y = silu(gate) * up, [M][N/2]); w4a16_gemm_decode_packed (M <= 4) for
-decode-packed and w4a16_gemm_small_packed (M <= 64; contraction and split-K
-reduce) for small-packed, both on weights repacked once by w4a16_grouped_pack
+Y = silu(gate) * up, [M][N/2]); w4a16_gemm_repacked (no workspace) for
+repacked, on weights repacked once by w4a16_repack, and
+w4a16_gemm_small_packed (M <= 64; contraction and split-K reduce) for
+small-packed, on weights repacked once by w4a16_grouped_pack
 (repack_ms_one_time).  Inputs are resident in HBM before the timed region starts.
 Copies of {X, qweight, scales, Y} rotate so that every step reads cold HBM
 (the copies together are at least twice the 256 MB Infinity Cache).  The K
@@ -51,17 +52,17 @@ MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "int4_weight_only_03_amd/csrc/"
 PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5,
-              "decode-packed": 6, "small-packed": 7}
+              "repacked": 6, "small-packed": 7}
 SPLIT_PATHS = ("split", "packed")
 # paths whose products are fp16 matrix instructions on two activation limbs
-LIMB_PATHS = ("split", "packed", "decode-packed", "small-packed")
+LIMB_PATHS = ("split", "packed", "repacked", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
-                "decode-packed": ["packed_gemv.hip", "gemv_common.h", "limbs.h"],
+                "repacked": ["packed_gemv.hip", "small_packed.hip", "gemv_common.h", "limbs.h"],
                 "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"]}
 
 
@@ -269,20 +270,20 @@ def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
         def step(i):
             x, _, _, y = sets[i % copies]
             pkg.w4a16_gemm_split_packed(x, packs[i % copies], wl.N, y, workspace=ws)
-    elif path == "decode-packed":
-        # the one-time repack into the grouped layout (one expert), timed on its own
-        packs = [pkg.w4a16_grouped_pack(q[None], s[None]) for (_, q, s, _) in sets]
+    elif path == "repacked":
+        # the one-time repack (w4a16_repack), timed on its own
+        packs = [pkg.w4a16_repack(q, s) for (_, q, s, _) in sets]
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        pkg.w4a16_grouped_pack(sets[0][1][None], sets[0][2][None], packs[0])
+        pkg.w4a16_repack(sets[0][1], sets[0][2], packs[0])
         ev1.record(stream)
         torch.cuda.synchronize()
         repack_ms = ev0.elapsed_time(ev1)
 
         def step(i):
             x, _, _, y = sets[i % copies]
-            pkg.w4a16_gemm_decode_packed(x, packs[i % copies], wl.N, y)
+            pkg.w4a16_gemm_repacked(x, packs[i % copies], wl.N, y)
     elif path == "small-packed":
         # the one-time repack into the grouped layout (one expert), timed on its own
         packs = [pkg.w4a16_grouped_pack(q[None], s[None]) for (_, q, s, _) in sets]
@@ -433,7 +434,7 @@ def main():
                         workloads.ORDER + list(workloads.MOE_WORKLOADS)))
     ap.add_argument("--path", default="auto",
                     help="kernel path(s), comma-separated: auto, gemv, tile, split, packed, "
-                         "swiglu, decode-packed, small-packed; grouped-MoE workloads run the grouped kernel on the "
+                         "swiglu, repacked, small-packed; grouped-MoE workloads run the grouped kernel on the "
                          "public layout, or with 'packed' on the repacked weights")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",

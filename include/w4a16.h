@@ -41,14 +41,23 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 #define W4A16_GROUP 32
 
-/* Largest supported extents.  K is limited so that one row of X stays below
- * 2 GiB; M and N so that grid indices fit in 32 bits. */
+/* Largest supported extents.  M and N are limited so that grid indices fit in
+ * 32 bits.  K is limited by accuracy: every kernel accumulates in fp32 (the
+ * pages' choice for fidelity, "The Silence of Success: A Single Line That
+ * Speaks Volumes", section "Assumptions Embedded in the Code"), and the
+ * rounding error of its longest summation chain grows with K.  With
+ * sign-coherent products (every x*w >= 0, the case where errors do not
+ * cancel) the longest chain of any kernel stays within the tolerance
+ * |dY| <= 1e-5 * sum|x*w| + 1e-6 up to K = 2^17 with a wide margin (the worst
+ * is the per-group chain of the matrix-core kernels, about 0.3 of the
+ * tolerance at K = 2^17); the tiled kernel adds its products in blocks of
+ * 8 groups for that reason.  Larger K is refused with W4A16_ERR_SHAPE. */
 #define W4A16_MAX_M ((int64_t)0x7fffffff)
 #define W4A16_MAX_N ((int64_t)0x7fffffff)
-#define W4A16_MAX_K ((int64_t)1 << 28)
+#define W4A16_MAX_K ((int64_t)1 << 17)
 
 /* Status codes (the int every entry point returns). */
 #define W4A16_OK 0
@@ -110,6 +119,56 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
                     void *stream);
 
 /*
+ * One-time repack of one weight matrix into a layout private to this
+ * library's kernels, and the GEMM on it (the pages describe no repack; the
+ * production kernel they plan to swap in brings layout and alignment
+ * constraints of its own, "The Quiet Commit: How a Single Documentation Edit
+ * Marks the Completion of a Major Engineering Milestone", section
+ * "Assumptions and Potential Mistakes").  The repack moves bits only and is
+ * meant to run once per weight, outside any timed or latency-critical path.
+ *
+ * The layout is that of w4a16_grouped_pack with one expert (E = 1): for
+ * 16-row tile t and 4-group step s (S4 = ceil(K/128) steps), block
+ * b = t*S4 + s holds 64 chunks of 16 bytes, chunk c + 16 R = word R of groups
+ * 4s..4s+3 of row 16t + c, and then, after all T16*S4 kilobytes of weights,
+ * the block's 16 x 4 scales (float (b*16 + c)*4 + q = scale of group 4s + q
+ * of row 16t + c).  Rows past N and groups past K/32 hold 0x88888888 (weight
+ * 0) and scale 0.  Every weight load of the kernels on it reads whole
+ * kilobytes already in matrix-instruction operand order.
+ */
+
+/* Bytes of the repacked weights of an N x K matrix: ceil(N/16) * ceil(K/128)
+ * * 1280 (qweight plus scales up to the padding of N to 16 rows and of the
+ * group count to a multiple of 4).  0 if the shape or group is invalid.
+ * Host only. */
+size_t w4a16_repacked_bytes(int64_t N, int64_t K, int32_t group);
+
+/* Repack qweight[N][K/8] and scales[N][K/32] (DEVICE memory) into `packed`
+ * (DEVICE memory owned by the caller, 16-byte aligned, at least
+ * w4a16_repacked_bytes(N, K, group) bytes, overlapping neither input).
+ * Enqueued on `stream`.  N == 0 is a no-op; W4A16_ERR_ARG for a NULL or
+ * overlapping pointer, negative extents, K == 0 or group != 32;
+ * W4A16_ERR_ALIGN for a misaligned qweight (16 bytes), scales (4) or packed
+ * (16); W4A16_ERR_SHAPE if K % 32 != 0 or an extent exceeds its limit. */
+int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int64_t N,
+                 int64_t K, int32_t group, void *stream);
+
+/* Y[M][N] = X[M][K] . dequant(W)^T with W repacked by w4a16_repack(..., N, K,
+ * ...).  No workspace and no allocation: for M <= 4 (when the activation limbs
+ * fit the kernel's LDS) a decode GEMV whose workgroups split K over their
+ * waves; otherwise one workgroup per 256 columns and 16 rows of X walks all
+ * of K in slices of up to 32 groups and adds the slices in order.  Both run
+ * on the fp16 matrix instructions with the arithmetic of w4a16_gemm_split
+ * (exact weight codes, two fp16 limbs of each activation prescaled by a power
+ * of two per row and K slice, fp32 accumulation; a row of X holding Inf or
+ * NaN gives NaN in that row of Y) within the tolerance of w4a16_gemm, and
+ * both are deterministic.  X (16-byte aligned), packed (16-byte aligned) and
+ * Y (4-byte aligned) are DEVICE memory; Y must not overlap X or packed.
+ * M == 0 or N == 0 is a no-op; otherwise errors as w4a16_gemm. */
+int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                        int64_t K, int32_t group, void *stream);
+
+/*
  * Fused gate/up projection with a SwiGLU epilogue, for the decode MLP whose
  * gate and up projections share one W4A16 matrix ("gate+up (2x2048)" in the
  * pages' decode configuration; SwiGLU is the engine's MLP activation):
@@ -168,8 +227,12 @@ size_t w4a16_grouped_pack_bytes(int64_t E, int64_t N, int64_t K);
  * (DEVICE memory, the layouts of w4a16_gemm_grouped) into the grouped matrix-
  * core kernel's private layout, `packed` (DEVICE memory owned by the caller,
  * 16-byte aligned, at least w4a16_grouped_pack_bytes(E, N, K) bytes,
- * overlapping no input): the optional repack into a kernel-private layout
- * that the pages allow for the weights; bits are moved only.  Layout, for
+ * overlapping no input): a one-time repack into a layout private to this
+ * library's kernels (the pages describe no repack; the production kernel
+ * they plan to swap in brings layout and alignment constraints of its own,
+ * "The Quiet Commit: How a Single Documentation Edit Marks the Completion of
+ * a Major Engineering Milestone", section "Assumptions and Potential
+ * Mistakes"); bits are moved only.  Layout, for
  * expert e, 16-row tile t (T16 = ceil(N/16) tiles) and 4-group step s
  * (S4 = ceil(K/128) steps), block b = (e*T16 + t)*S4 + s:
  *   bytes [0, E*T16*S4*1024): at b*64 + l chunks of 16 bytes, l = c + 16 R:
@@ -198,27 +261,6 @@ int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
                               const int32_t *expert_offsets, const void *packed, float *Y,
                               int64_t T, int64_t R, int64_t E, int64_t N, int64_t K,
                               int32_t group, void *stream);
-
-/*
- * Decode GEMV on packed weights: Y[M][N] = X[M][K] . dequant(W)^T for
- * 1 <= M <= 4, W packed once by w4a16_grouped_pack(qweight, scales, 1, N, K,
- * ...) (a single expert).  The arithmetic of w4a16_gemm_split (exact weight
- * codes, two fp16 limbs of each prescaled activation, fp32 accumulation; a
- * row of X holding Inf or NaN gives NaN in that row of Y), within the
- * tolerance of w4a16_gemm.  The pages' decode steps are memory-bound GEMVs;
- * with the packed layout every weight load reads a contiguous kilobyte.  One
- * workgroup per 16 rows of W splits K over its waves and adds their partial
- * sums in a fixed order (deterministic).  X, packed (16-byte aligned) and Y
- * are DEVICE memory; Y must not overlap X or packed.  M == 0 or N == 0 is a
- * no-op; M > 4, or a K whose activation limbs (4*M*K bytes) do not fit the
- * kernel's LDS budget (w4a16_decode_packed_supported), is W4A16_ERR_SHAPE;
- * otherwise errors as w4a16_gemm.
- */
-int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
-                             int64_t K, int32_t group, void *stream);
-
-/* 1 if w4a16_gemm_decode_packed takes M rows with this K, else 0.  Host only. */
-int w4a16_decode_packed_supported(int64_t M, int64_t K);
 
 /*
  * Small-M GEMM on packed weights: Y[M][N] = X[M][K] . dequant(W)^T for
@@ -321,9 +363,10 @@ size_t w4a16_split_pack_bytes(int64_t N, int64_t K);
  * One-time repack of qweight[N][K/8] and scales[N][K/32] (DEVICE memory, the
  * layouts above) into the split path's kernel-private layout, `packed` (DEVICE
  * memory owned by the caller, 16-byte aligned, at least
- * w4a16_split_pack_bytes(N, K) bytes, overlapping no input).  The optional
- * repack into a kernel-private layout that the pages allow for the weights;
- * it moves bits only (the weights and scales are copied unchanged).  Layout,
+ * w4a16_split_pack_bytes(N, K) bytes, overlapping no input): a one-time
+ * repack into a layout private to this library's kernels (as for
+ * w4a16_grouped_pack); it moves bits only (the weights and scales are copied
+ * unchanged).  Layout,
  * for slab s of 64 rows and stage t of 2 groups (S = ceil(N/64) slabs,
  * T = ceil(K/64) stages):
  *   bytes [0, S*T*2048): at ((s*T + t)*2 + g)*64 + r chunks of 16 bytes, the

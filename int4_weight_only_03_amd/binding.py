@@ -68,9 +68,12 @@ _SIGS = {
     "w4a16_grouped_kernel": ([ctypes.c_int64] * 5, ctypes.c_int),
     "w4a16_gemv_kernel": ([ctypes.c_int64] * 3, ctypes.c_int),
     "w4a16_grouped_pack_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
-    "w4a16_decode_packed_supported": ([ctypes.c_int64] * 2, ctypes.c_int),
-    "w4a16_gemm_decode_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
-                                 [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_repacked_bytes": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int32], ctypes.c_size_t),
+    "w4a16_repack": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int32,
+                                                                    ctypes.c_void_p],
+                     ctypes.c_int),
+    "w4a16_gemm_repacked": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
+                            [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_small_packed_workspace_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
     "w4a16_gemm_small_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
                                 [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
@@ -290,31 +293,56 @@ def w4a16_gemm_grouped_packed(X, token_index, expert_offsets, packed, E: int, N:
     return Y
 
 
-def w4a16_decode_packed_supported(M: int, K: int) -> bool:
-    return bool(load().w4a16_decode_packed_supported(M, K))
+def w4a16_repacked_bytes(N: int, K: int) -> int:
+    return int(load().w4a16_repacked_bytes(N, K, GROUP))
 
 
-def w4a16_gemm_decode_packed(X, packed, N: int, Y=None, stream=None):
-    """Decode GEMV (M <= 4) on weights from w4a16_grouped_pack of one expert
-    ([1][N][K/8] qweight, [1][N][K/32] scales), N output rows."""
+def w4a16_repack(qweight, scales, packed=None, stream=None):
+    """One-time repack of device qweight [N][K/8] and scales [N][K/32] into the
+    library's private layout (uint8 tensor of w4a16_repacked_bytes(N, K) bytes)."""
+    import torch
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float32, "scales")
+    if qweight.dim() != 2 or scales.dim() != 2:
+        raise ValueError("qweight and scales must be 2-D")
+    N, K8 = qweight.shape
+    K = 8 * K8
+    if tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError(f"shapes disagree: qweight {tuple(qweight.shape)}, "
+                         f"scales {tuple(scales.shape)}")
+    need = w4a16_repacked_bytes(N, K) if N else 0
+    if packed is None:
+        packed = torch.empty(max(need, 1), dtype=torch.uint8, device=qweight.device)
+    packed = _dev(packed, torch.uint8, "packed")
+    if packed.numel() < need:
+        raise ValueError("packed buffer smaller than w4a16_repacked_bytes(N, K)")
+    st = load().w4a16_repack(qweight.data_ptr(), scales.data_ptr(), packed.data_ptr(), N, K,
+                             GROUP, _stream_ptr(stream, qweight.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_repack")
+    return packed
+
+
+def w4a16_gemm_repacked(X, packed, N: int, Y=None, stream=None):
+    """Y = X . dequant(W)^T with W repacked by w4a16_repack (N output rows)."""
     import torch
     X = _dev(X, torch.float32, "X")
     packed = _dev(packed, torch.uint8, "packed")
     if X.dim() != 2:
         raise ValueError("X must be 2-D")
     M, K = X.shape
-    if packed.numel() < w4a16_grouped_pack_bytes(1, N, K):
-        raise ValueError("packed buffer smaller than w4a16_grouped_pack_bytes(1, N, K)")
+    if N and packed.numel() < w4a16_repacked_bytes(N, K):
+        raise ValueError("packed buffer smaller than w4a16_repacked_bytes(N, K)")
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     else:
         Y = _dev(Y, torch.float32, "Y")
         if tuple(Y.shape) != (M, N):
             raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
-    st = load().w4a16_gemm_decode_packed(X.data_ptr(), packed.data_ptr(), Y.data_ptr(), M, N, K,
-                                         GROUP, _stream_ptr(stream, X.device))
+    st = load().w4a16_gemm_repacked(X.data_ptr(), packed.data_ptr(), Y.data_ptr(), M, N, K,
+                                    GROUP, _stream_ptr(stream, X.device))
     if st != W4A16_OK:
-        raise W4A16Error(st, "w4a16_gemm_decode_packed")
+        raise W4A16Error(st, "w4a16_gemm_repacked")
     return Y
 
 

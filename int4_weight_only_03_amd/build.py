@@ -25,8 +25,10 @@ DEVICE_SOURCES = ["gemv.hip", "gemv_mfma.hip", "tile.hip", "split.hip", "grouped
                   "small_packed.hip"]
 HOST_SOURCES = ["w4a16_api.cpp", "w4a16_io.cpp"]
 # per-source options: the split path's MFMA results stay in VGPRs (the scale
-# FMAs read them directly, no accumulator-register copies)
-EXTRA = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# FMAs read them directly, no accumulator-register copies); so do the tiled
+# kernel's block sums, which are added to running totals in VGPRs
+EXTRA = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

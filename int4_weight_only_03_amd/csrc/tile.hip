@@ -22,6 +22,13 @@
 // side by side and KS copies of that arrangement splitting the groups; the KS
 // partial tiles are summed in LDS in a fixed order (deterministic, no atomics).
 // The next group's raw loads are issued before the current group's MFMAs.
+//
+// Accumulation order.  The MFMAs of kAccGroups consecutive groups (16 each)
+// accumulate from zero into a block sum, and each block sum is added to the
+// running total with one fp32 add.  A single chain over all of K would let
+// the rounding error of sign-coherent products (every x*w >= 0) grow with the
+// chain length until it leaves the tolerance near K = 2^17; with blocks of
+// 8 groups the longest chain is 128 MFMAs plus K/256 block adds.
 
 #include "w4a16_internal.h"
 
@@ -31,6 +38,8 @@ namespace w4a16 {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kAccGroups = 8;  // groups per block sum (see "Accumulation order")
 
 template <int WM, int WN, int BWM, int BWN, int KS>
 __global__ void __launch_bounds__(64 * BWM * BWN * KS)
@@ -72,13 +81,14 @@ tile_w4a16(const float *__restrict__ X, const uint32_t *__restrict__ qw,
     srow[b] = sc + long(n) * G;
   }
 
-  floatx16 acc[WM][WN];
+  floatx16 acc[WM][WN];  // block sum of the current kAccGroups groups
+  floatx16 tot[WM][WN];  // sum of the finished blocks
 #pragma unroll
   for (int a = 0; a < WM; ++a)
 #pragma unroll
     for (int b = 0; b < WN; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = tot[a][b][r] = 0.0f;
 
   float4 xa[WM][4];
   uint2 wq[WN];
@@ -137,6 +147,19 @@ tile_w4a16(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
         for (int b = 0; b < WN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(xc[a][i], wc[b][i], acc[a][b], 0, 0, 0);
+    // at the end of each block of kAccGroups groups (and of the range) the
+    // block sum joins the total and the next block starts from zero
+    if ((g - g0) % kAccGroups == kAccGroups - 1 || g + 1 == g1) {
+#pragma unroll
+      for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            tot[a][b][r] += acc[a][b][r];
+            acc[a][b][r] = 0.0f;
+          }
+    }
   }
 
   if constexpr (KS > 1) {
@@ -151,7 +174,7 @@ tile_w4a16(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             red[((((wk - 1) * WAVES_MN + wmn) * WM + a) * WN + b) * 1024 + r * 64 + lane] =
-                acc[a][b][r];
+                tot[a][b][r];
     }
     __syncthreads();
     if (wk != 0) return;
@@ -162,7 +185,7 @@ tile_w4a16(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         for (int b = 0; b < WN; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            acc[a][b][r] += red[((((k - 1) * WAVES_MN + wmn) * WM + a) * WN + b) * 1024 + r * 64 + lane];
+            tot[a][b][r] += red[((((k - 1) * WAVES_MN + wmn) * WM + a) * WN + b) * 1024 + r * 64 + lane];
   }
 
 #pragma unroll
@@ -174,7 +197,7 @@ tile_w4a16(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m_base + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) Y[long(m) * N + n] = acc[a][b][r];
+        if (m < M) Y[long(m) * N + n] = tot[a][b][r];
       }
     }
 }

@@ -188,26 +188,47 @@ int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
-int w4a16_decode_packed_supported(int64_t M, int64_t K) {
-  if (M < 1 || K <= 0 || K % W4A16_GROUP != 0 || K > W4A16_MAX_K) return 0;
-  return w4a16::decode_packed_supported(int(std::min<int64_t>(M, 5)), int(K)) ? 1 : 0;
+size_t w4a16_repacked_bytes(int64_t N, int64_t K, int32_t group) {
+  if (group != W4A16_GROUP) return 0;
+  return w4a16_grouped_pack_bytes(1, N, K);
 }
 
-int w4a16_gemm_decode_packed(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
-                             int64_t K, int32_t group, void *stream) {
+int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int64_t N, int64_t K,
+                 int32_t group, void *stream) {
+  // the grouped layout with a single expert; the caller provides at least
+  // w4a16_repacked_bytes(N, K, group) bytes
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (N == 0) return W4A16_OK;
+  if (!qweight || !scales || !packed) return W4A16_ERR_ARG;
+  if (!aligned(qweight, 16) || !aligned(scales, 4) || !aligned(packed, 16)) return W4A16_ERR_ALIGN;
+  const size_t need = w4a16::grouped_pack_bytes(1, int(N), int(K));
+  const size_t bq = size_t(N) * size_t(K) / 2, bs = size_t(N) * size_t(K / W4A16_GROUP) * 4;
+  if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
+    return W4A16_ERR_ARG;
+  hipError_t e = w4a16::launch_grouped_pack(qweight, scales, packed, 1, int(N), int(K),
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
+                        int64_t K, int32_t group, void *stream) {
   if (group != W4A16_GROUP) return W4A16_ERR_ARG;
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
   if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
   if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
   if (M == 0 || N == 0) return W4A16_OK;
-  if (!w4a16::decode_packed_supported(int(std::min<int64_t>(M, 5)), int(K))) return W4A16_ERR_SHAPE;
   if (!X || !packed || !Y) return W4A16_ERR_ARG;
   if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4)) return W4A16_ERR_ALIGN;
   const size_t bx = size_t(M) * size_t(K) * 4, by = size_t(M) * size_t(N) * 4;
   const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
-  hipError_t e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K),
-                                             reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
+                     ? w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s)
+                     : w4a16::launch_small_packed_loop(X, packed, Y, int(M), int(N), int(K), s);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

@@ -70,6 +70,10 @@ bool small_packed_supported(int M);
 size_t small_packed_workspace_bytes(int M, int N, int K);
 hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
                                void *workspace, hipStream_t stream);
+// the same GEMM for any M >= 1 with no workspace: each workgroup walks every
+// K slice of its (column group, row chunk) and adds the slices in order
+hipError_t launch_small_packed_loop(const float *X, const void *packed, float *Y, int M, int N,
+                                    int K, hipStream_t stream);
 // the packed layout of the grouped path: bytes, repack, the packed GEMM and
 // whether a shape can use it
 size_t grouped_pack_bytes(int E, int N, int K);

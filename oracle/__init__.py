@@ -20,6 +20,7 @@ from .w4a16_ref import (  # noqa: F401
     gemm_entries,
     bound,
     compare,
+    compare_to,
     compare_entries,
     pack_split,
     silu,

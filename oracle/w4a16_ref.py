@@ -38,11 +38,12 @@ Readings taken where the pages are silent (each is listed in the design doc):
   or so tiny that max|w|/7 underflows) gets q = 0 everywhere.
 * Non-finite weights are rejected; K % 32 != 0 is rejected (no padding).
 * Dequantized weight = fl32((nibble - 8) * scale), one rounded fp32 multiply.
-* Repack: the pages allow an optional one-time repack of the weights into a
-  kernel-private layout.  ``pack_split`` writes the library's split-path
-  layout from its index formula (64-row slabs, stages of 2 groups, zero code
-  and zero scale as padding); it only moves bits, so the library's repack
-  must match it byte for byte.
+* Repack: the pages describe no repack step; the library adds an optional
+  one-time repack of the weights into layouts private to its kernels.
+  ``pack_split`` writes the split-path layout from its index formula (64-row
+  slabs, stages of 2 groups, zero code and zero scale as padding) and
+  ``pack_grouped`` the grouped one; they only move bits, so the library's
+  repacks must match them byte for byte.
 * Grouped (MoE) GEMM: routed slot r of expert e is the product of token
   token_index[r] with expert e's weights (the pages run the MoE experts
   through the INT4 path); ``grouped_gemm`` applies ``gemm`` expert by expert
@@ -336,6 +337,14 @@ def _verdict(Y, Yref, T) -> dict:
         "finite": finite,
         "n": int(ratio.size),
     }
+
+
+def compare_to(Y: np.ndarray, Yref: np.ndarray, T: np.ndarray) -> dict:
+    """The acceptance verdict of Y against a Y_ref = gemm(...) and T = abs_gemm(...)
+    computed once (for large problems checked on several paths)."""
+    if np.shape(Y) != np.shape(Yref):
+        raise ValueError(f"Y shape {np.shape(Y)} != {np.shape(Yref)}")
+    return _verdict(Y, Yref, T)
 
 
 def compare(Y: np.ndarray, X: np.ndarray, qweight: np.ndarray, scales: np.ndarray) -> dict:

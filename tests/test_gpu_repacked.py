@@ -1,0 +1,124 @@
+"""GPU parity of the repack entry points against the oracle, through the C ABI:
+w4a16_repack must write the oracle's pack_grouped layout (one expert) byte for
+byte, and w4a16_gemm_repacked (decode GEMV for M <= 4 when its LDS holds the
+activation limbs, otherwise the looped small-M kernel) must meet the tolerance
+on every output."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_only_03_amd import binding  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run(X, qw, sc, dev, Y=None):
+    N = qw.shape[0]
+    packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
+    out = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, N, Y)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 128), (17, 96), (130, 224), (300, 7168)])
+def test_repack_matches_oracle_bytes(dev, N, K):
+    say(f"repack bytes N={N} K={K}")
+    _, W = workloads.random_case(1, N, K, seed=N * 3 + K)
+    qw, sc = oracle.quantize(W)
+    got = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev)).cpu().numpy()
+    want = oracle.pack_grouped(qw[None], sc[None])
+    assert got.size == binding.w4a16_repacked_bytes(N, K) == want.size
+    assert np.array_equal(got, want)
+
+
+SHAPES = [
+    # decode kernel (M <= 4, limbs fit its LDS)
+    (1, 512, 256), (2, 70, 224), (3, 33, 96), (4, 129, 512), (1, 16, 32), (1, 100, 38144),
+    (4, 64, 9344), (2, 300, 7168),
+    # looped small-M kernel: M > 4, or K too long for the decode kernel's LDS
+    (1, 40, 38176), (4, 20, 9376), (5, 17, 32), (8, 100, 1056), (17, 70, 160), (33, 45, 4128),
+    (63, 33, 96), (64, 300, 7168), (65, 129, 224), (130, 200, 320), (300, 260, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_repacked_shapes(dev, M, N, K):
+    say(f"repacked M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M * 17 + N + K)
+    qw, sc = oracle.quantize(W)
+    v = oracle.compare(run(X, qw, sc, dev), X, qw, sc)
+    say(f"  max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_gate_up", "decode_down", "verify_tree"])
+def test_repacked_workloads_every_output(dev, name):
+    say(f"repacked {name}")
+    X, W = workloads.make(name)
+    qw, sc = oracle.quantize(W)
+    v = oracle.compare(run(X, qw, sc, dev), X, qw, sc)
+    say(f"  max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 48, 512), (40, 48, 512)])
+def test_repacked_integer_exact(dev, M, N, K):
+    rng = np.random.default_rng(8 + M)
+    X = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.5), np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+@pytest.mark.parametrize("M", [3, 21])
+def test_repacked_guard_band_and_determinism(dev, M):
+    N, K = 45, 160
+    X, W = workloads.random_case(M, N, K, seed=4)
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    a = run(X, qw, sc, dev, Y)
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    b = run(X, qw, sc, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert oracle.compare(a, X, qw, sc)["ok"]
+
+
+def test_repacked_nonfinite_row(dev):
+    # a row holding Inf or NaN turns its outputs to NaN; the other rows are unaffected
+    M, N, K = 6, 40, 256
+    X, W = workloads.random_case(M, N, K, seed=12)
+    X[1, 5] = np.inf
+    X[4, 200] = np.nan
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, dev)
+    assert np.all(np.isnan(Y[1])) and np.all(np.isnan(Y[4]))
+    keep = [0, 2, 3, 5]
+    assert oracle.compare(Y[keep], X[keep], qw, sc)["ok"]

@@ -23,10 +23,11 @@ def test_exports_every_declared_symbol(lib):
     assert {"w4a16_gemm", "w4a16_quantize", "w4a16_gemm_path", "w4a16_status_str",
             "w4a16_abi_version", "w4a16_select_path", "w4a16_gemm_split",
             "w4a16_split_workspace_bytes", "w4a16_split_pack", "w4a16_split_pack_bytes",
-            "w4a16_gemm_split_packed", "w4a16_gemm_swiglu", "w4a16_gemm_grouped"} <= set(names)
+            "w4a16_gemm_split_packed", "w4a16_gemm_swiglu", "w4a16_gemm_grouped",
+            "w4a16_repacked_bytes", "w4a16_repack", "w4a16_gemm_repacked"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.w4a16_abi_version() == 1
+    assert lib.w4a16_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -63,7 +64,8 @@ def test_select_path(lib):
 
 # ------------------------------------------------------------------ quantize
 
-@pytest.mark.parametrize("name", ["tiny", "decode_down", "decode_gate_up"])
+@pytest.mark.parametrize("name", ["tiny", "decode_down", "decode_gate_up", "verify_tree",
+                                  "prefill"])
 def test_quantize_bit_exact_with_oracle(lib, name):
     W = workloads.make_w(name)
     qa, sa = binding.w4a16_quantize(W)
@@ -130,7 +132,10 @@ def test_gemm_rejects_bad_arguments_synchronously(lib):
     assert _call(lib, X_, Q_, S_, Y_, 1, -8, 64) == ARG
     assert _call(lib, X_, Q_, S_, Y_, 1, 8, 48) == SHAPE
     assert _call(lib, X_, Q_, S_, Y_, 1, 8, 100) == SHAPE
-    assert _call(lib, X_, Q_, S_, Y_, 1, 8, (1 << 28) + 32) == SHAPE
+    assert _call(lib, X_, Q_, S_, Y_, 1, 8, (1 << 17) + 32) == SHAPE
+    # the largest K passes validation (M = 0: nothing is launched)
+    assert _call(lib, None, None, None, None, 0, 8, 1 << 17) == OK
+    assert _call(lib, None, None, None, None, 0, 8, (1 << 17) + 32) == SHAPE
     assert _call(lib, X_, Q_, S_, Y_, 1 << 31, 8, 64) == SHAPE
     assert _call(lib, None, Q_, S_, Y_, 1, 8, 64) == ARG
     assert _call(lib, X_, None, S_, Y_, 1, 8, 64) == ARG
@@ -326,22 +331,45 @@ def test_grouped_packed_gemm_errors(lib):
     assert g(None, None, None, r=0) == OK
 
 
-def test_decode_packed_errors(lib):
+def test_repack_trio_errors(lib):
+    """The repack entry points: sizes, and argument errors before any launch."""
     P_ = BASE + (5 << 32)
-    g = lambda x, p, y, m=1, n=64, k=256, group=32: lib.w4a16_gemm_decode_packed(
+    # ceil(N/16) * ceil(K/128) * 1280 bytes: 16-row tiles, 4-group steps of 1 KB
+    # of weights and 256 B of scales
+    assert lib.w4a16_repacked_bytes(4096, 7168, 32) == 256 * 56 * 1280
+    assert lib.w4a16_repacked_bytes(17, 96, 32) == 2 * 1 * 1280
+    assert lib.w4a16_repacked_bytes(4096, 7168, 16) == 0
+    assert lib.w4a16_repacked_bytes(4096, 48, 32) == 0
+    assert lib.w4a16_repacked_bytes(0, 7168, 32) == 0
+    assert lib.w4a16_repacked_bytes(64, (1 << 17) + 32, 32) == 0
+    r = lambda q, s_, p, n=64, k=256, group=32: lib.w4a16_repack(q, s_, p, n, k, group, None)
+    assert r(Q_, S_, P_, k=48) == SHAPE
+    assert r(Q_, S_, P_, k=(1 << 17) + 32) == SHAPE
+    assert r(Q_, S_, P_, group=16) == ARG
+    assert r(Q_, S_, P_, n=-1) == ARG
+    assert r(None, S_, P_) == ARG
+    assert r(Q_, S_, None) == ARG
+    assert r(Q_ + 4, S_, P_) == ALIGN
+    assert r(Q_, S_ + 2, P_) == ALIGN
+    assert r(Q_, S_, P_ + 4) == ALIGN
+    assert r(Q_, S_, Q_ + 64) == ARG                      # packed overlaps qweight
+    assert r(Q_, S_, S_ + 64) == ARG                      # packed overlaps scales
+    assert r(None, None, None, n=0) == OK
+    g = lambda x, p, y, m=1, n=64, k=256, group=32: lib.w4a16_gemm_repacked(
         x, p, y, m, n, k, group, None)
-    assert g(X_, P_, Y_, m=5) == SHAPE
-    assert g(X_, P_, Y_, k=38176) == SHAPE
     assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_, Y_, k=(1 << 17) + 32) == SHAPE
     assert g(X_, P_ + 4, Y_) == ALIGN
     assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(X_, P_, Y_ + 2) == ALIGN
     assert g(None, P_, Y_) == ARG
+    assert g(X_, None, Y_) == ARG
     assert g(X_, P_, X_ + 64) == ARG                      # Y overlaps X
     assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
     assert g(X_, P_, Y_, group=16) == ARG
+    assert g(X_, P_, Y_, m=-1) == ARG
     assert g(None, None, None, m=0) == OK
-    assert lib.w4a16_decode_packed_supported(1, 7168) == 1
-    assert lib.w4a16_decode_packed_supported(0, 7168) == 0
+    assert g(None, None, None, n=0) == OK
 
 
 def test_small_packed_errors(lib):

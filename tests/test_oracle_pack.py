@@ -1,7 +1,8 @@
 """Pins of the oracle's split-path packed layout (pack_split / unpack_split).
 
-The layout is the library's own (the pages allow a one-time repack into a
-kernel-private layout); it moves bits only.  Pinned by: a round trip that
+The layout is the library's own (the pages describe no repack; the library
+adds a one-time repack into layouts private to its kernels); it moves bits
+only.  Pinned by: a round trip that
 restores every input bit, the padding contents and size, and a GEMM computed
 by plain loops that fetch each weight and scale through the packed bytes,
 which must equal the oracle's product of the unpacked operands exactly.

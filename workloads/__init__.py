@@ -176,6 +176,14 @@ def random_case(M: int, N: int, K: int, seed: int, x_kind: str = "gauss",
     return _draw_x(rng, x_kind, M, K), _draw_w(rng, w_kind, N, K)
 
 
+def coherent_case(M: int, N: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Sign-coherent (X, W): the magnitudes of a random_case draw, so every
+    activation is >= 0 and every weight quantizes to a code >= 8 (every
+    product x * w >= 0 and rounding errors of a sum cannot cancel)."""
+    x, w = random_case(M, N, K, seed)
+    return np.abs(x), np.abs(w)
+
+
 def integer_case(M: int, N: int, K: int, seed: int, lo: int = -8, hi: int = 8):
     """Integer-valued X in [lo, hi] and raw nibbles in [0, 15], as float32 / uint8.
 
