@@ -21,9 +21,10 @@
  *
  * Memory and ownership: every pointer argument of w4a16_gemm* is a DEVICE
  * pointer owned by the caller; w4a16_quantize takes HOST pointers.  The library
- * allocates nothing, keeps no state between calls and is safe to call from
- * several host threads at once.  Results of calls that write the same Y
- * buffer concurrently are undefined.
+ * allocates nothing and keeps no state between calls, apart from the fixed
+ * device scratch array of w4a16_gemm_small_packed_noalloc; every other entry
+ * point is safe to call from several host threads at once.  Results of calls
+ * that write the same Y buffer concurrently are undefined.
  *
  * Errors: argument problems are detected on the host, synchronously, before
  * anything is launched, and reported as a status code (Y untouched).  Work is
@@ -70,6 +71,8 @@ extern "C" {
 #define W4A16_ERR_HIP 5       /* the HIP runtime refused a launch */
 #define W4A16_ERR_IO 6        /* w4a16_load_quantized / w4a16_save_quantized: a file cannot be
                                  opened, read or written, or its size is not the expected one */
+#define W4A16_ERR_SCRATCH 7   /* w4a16_gemm_small_packed_noalloc: the call needs more scratch
+                                 than the library's fixed W4A16_NOALLOC_SCRATCH_BYTES */
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
@@ -289,6 +292,27 @@ int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_
 /* Workspace bytes w4a16_gemm_small_packed needs (0 when K is not split, or
  * when the shape is not accepted).  Host only. */
 size_t w4a16_small_packed_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w4a16_gemm_small_packed for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels, the same plan and the same result bit for
+ * bit, with the split-K partials in a scratch array the library holds in
+ * device memory instead of a caller workspace.  The array is
+ * W4A16_NOALLOC_SCRATCH_BYTES per device, a file-scope device variable that
+ * each GPU the library runs on keeps until the process ends (its address is
+ * looked up once per device, on the first call there); no call allocates or
+ * frees anything.  Every call on one GPU shares that GPU's array and leaves
+ * its last partials there: calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  A shape
+ * whose partials, w4a16_small_packed_workspace_bytes(M, N, K), exceed
+ * W4A16_NOALLOC_SCRATCH_BYTES is refused with W4A16_ERR_SCRATCH before any GPU
+ * work; otherwise arguments and errors as w4a16_gemm_small_packed (no
+ * workspace arguments).
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y, int64_t M,
+                                    int64_t N, int64_t K, int32_t group, void *stream);
 
 /* Kernels behind w4a16_gemm_grouped. */
 #define W4A16_GROUPED_MFMA 1  /* matrix cores, split-path arithmetic; up to 4096 experts

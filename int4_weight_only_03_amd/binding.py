@@ -75,6 +75,8 @@ _SIGS = {
     "w4a16_gemm_repacked": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
                             [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_small_packed_workspace_bytes": ([ctypes.c_int64] * 3, ctypes.c_size_t),
+    "w4a16_gemm_small_packed_noalloc": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
+                                        [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "w4a16_gemm_small_packed": ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 +
                                 [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p], ctypes.c_int),
@@ -378,6 +380,34 @@ def w4a16_gemm_small_packed(X, packed, N: int, Y=None, workspace=None, stream=No
                                         _stream_ptr(stream, X.device))
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemm_small_packed")
+    return Y
+
+
+W4A16_ERR_SCRATCH = 7
+W4A16_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w4a16_gemm_small_packed_noalloc(X, packed, N: int, Y=None, stream=None):
+    """w4a16_gemm_small_packed with the split-K partials in the library's fixed
+    device scratch (no workspace, nothing allocated by the library)."""
+    import torch
+    X = _dev(X, torch.float32, "X")
+    packed = _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    M, K = X.shape
+    if packed.numel() < w4a16_grouped_pack_bytes(1, N, K):
+        raise ValueError("packed buffer smaller than w4a16_grouped_pack_bytes(1, N, K)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        Y = _dev(Y, torch.float32, "Y")
+        if tuple(Y.shape) != (M, N):
+            raise ValueError(f"Y shape {tuple(Y.shape)} != {(M, N)}")
+    st = load().w4a16_gemm_small_packed_noalloc(X.data_ptr(), packed.data_ptr(), Y.data_ptr(),
+                                                M, N, K, GROUP, _stream_ptr(stream, X.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemm_small_packed_noalloc")
     return Y
 
 

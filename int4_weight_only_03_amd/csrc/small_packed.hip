@@ -47,6 +47,7 @@
 #include "limbs.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace w4a16 {
 namespace {
@@ -438,6 +439,36 @@ hipError_t launch_small_packed_loop(const float *X, const void *packed, float *Y
   const float *ps = reinterpret_cast<const float *>(pw + long(p.tiles) * p.S4 * 64);
   run_small<1, true>(p, X, pw, ps, Y, nullptr, M, N, K, stream);
   return hipGetLastError();
+}
+
+// Fixed scratch of the allocation-free entry point: the split-K partials of
+// one call.  Each device the library runs on holds its own copy for the life
+// of the process.  Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol); it passes the device address
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace w4a16

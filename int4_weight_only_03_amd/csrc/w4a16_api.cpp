@@ -67,6 +67,7 @@ const char *w4a16_status_str(int status) {
     case W4A16_ERR_NONFINITE: return "non-finite weight";
     case W4A16_ERR_HIP: return "HIP runtime error";
     case W4A16_ERR_IO: return "weight file cannot be read or written, or has the wrong size";
+    case W4A16_ERR_SCRATCH: return "the call needs more than the library's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -259,6 +260,28 @@ int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_
       return W4A16_ERR_ARG;
   }
   hipError_t e = w4a16::launch_small_packed(X, packed, Y, int(M), int(N), int(K), workspace,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y, int64_t M,
+                                    int64_t N, int64_t K, int32_t group, void *stream) {
+  static_assert(W4A16_NOALLOC_SCRATCH_BYTES == w4a16::kNoAllocScratchBytes, "scratch size");
+  if (group != W4A16_GROUP) return W4A16_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_ARG;
+  if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+  if (M > W4A16_SMALL_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return W4A16_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!X || !packed || !Y) return W4A16_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 4)) return W4A16_ERR_ALIGN;
+  const size_t bx = size_t(M) * size_t(K) * 4, by = size_t(M) * size_t(N) * 4;
+  const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
+  if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
+  const size_t need = w4a16::small_packed_workspace_bytes(int(M), int(N), int(K));
+  if (need > W4A16_NOALLOC_SCRATCH_BYTES) return W4A16_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (need > 0 && w4a16::noalloc_scratch(&ws) != hipSuccess) return W4A16_ERR_HIP;
+  hipError_t e = w4a16::launch_small_packed(X, packed, Y, int(M), int(N), int(K), ws,
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }

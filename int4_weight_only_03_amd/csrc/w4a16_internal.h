@@ -70,6 +70,11 @@ bool small_packed_supported(int M);
 size_t small_packed_workspace_bytes(int M, int N, int K);
 hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
                                void *workspace, hipStream_t stream);
+// The allocation-free form's scratch: a file-scope device array of
+// kNoAllocScratchBytes per device; noalloc_scratch gives its device address
+// on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
 // the same GEMM for any M >= 1 with no workspace: each workgroup walks every
 // K slice of its (column group, row chunk) and adds the slices in order
 hipError_t launch_small_packed_loop(const float *X, const void *packed, float *Y, int M, int N,

@@ -15,7 +15,7 @@ import oracle
 import workloads
 from int4_weight_only_03_amd import binding
 
-OK, ARG, SHAPE, ALIGN, NONFINITE, HIP = 0, 1, 2, 3, 4, 5
+OK, ARG, SHAPE, ALIGN, NONFINITE, HIP, IO, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def test_exports_every_declared_symbol(lib):
@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     seen = set()
-    for code in (OK, ARG, SHAPE, ALIGN, NONFINITE, HIP):
+    for code in (OK, ARG, SHAPE, ALIGN, NONFINITE, HIP, IO, SCRATCH):
         text = binding.w4a16_status_str(code)
         assert text and text not in seen
         seen.add(text)
@@ -396,5 +396,26 @@ def test_small_packed_errors(lib):
     assert g(X_, P_, Y_, wsb=need - 4) == ARG             # too small
     assert g(X_, P_, Y_, ws=X_) == ARG                    # overlaps X
     assert g(X_, P_, Y_, ws=Y_) == ARG                    # overlaps Y
+    assert g(None, None, None, m=0) == OK
+    assert g(None, None, None, n=0) == OK
+
+
+def test_small_packed_noalloc_errors(lib):
+    """Refusals of the allocation-free entry point, all before any GPU work."""
+    P_ = BASE + (5 << 32)
+    g = lambda x, p, y, m=64, n=4096, k=7168, group=32: \
+        lib.w4a16_gemm_small_packed_noalloc(x, p, y, m, n, k, group, None)
+    # partials beyond the fixed 64 MiB: 7 K slices x 64 x 65536 floats
+    assert lib.w4a16_small_packed_workspace_bytes(64, 65536, 7168) > 64 << 20
+    assert lib.w4a16_small_packed_workspace_bytes(64, 32768, 7168) <= 64 << 20
+    assert g(X_, P_, Y_, n=65536) == SCRATCH
+    assert g(X_, P_, Y_, m=65) == SHAPE
+    assert g(X_, P_, Y_, k=48) == SHAPE
+    assert g(X_, P_, Y_, group=16) == ARG
+    assert g(X_ + 4, P_, Y_) == ALIGN
+    assert g(X_, P_ + 4, Y_) == ALIGN
+    assert g(None, P_, Y_) == ARG
+    assert g(X_, P_, X_ + 64) == ARG                      # Y overlaps X
+    assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
     assert g(None, None, None, m=0) == OK
     assert g(None, None, None, n=0) == OK
