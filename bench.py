@@ -1,30 +1,43 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A16 group-quantized GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME[,NAME]|all]
-                    [--path auto|gemv|tile|split|packed|swiglu|repacked|small-packed[,...]]
-                    [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-cpu]
+    python bench.py --workload NAME[,NAME]|all [--path P[,P]] [--steps K] [--no-cpu]
 
-A step is one call of the chosen entry point (the whole hot path: validate,
-launch, unpack + dequant + contraction + reduction + store) on one batch of
-synthetic input: w4a16_gemm / w4a16_gemm_path for auto, gemv and tile;
-w4a16_gemm_split (activation prep, fp16-MFMA contraction, split-K reduce) for
-split; w4a16_gemm_split_packed for packed, whose one-time weight repack runs
-before the timed region and is reported on its own (repack_ms_one_time);
-w4a16_gemm_swiglu for swiglu (the workload's W read as gate rows then up rows,
-Y = silu(gate) * up, [M][N/2]); w4a16_gemm_repacked (no workspace) for
-repacked, on weights repacked once by w4a16_repack, and
-w4a16_gemm_small_packed (M <= 64; contraction and split-K reduce) for
-small-packed, on weights repacked once by w4a16_grouped_pack
-(repack_ms_one_time).  Inputs are resident in HBM before the timed region starts.
-Copies of {X, qweight, scales, Y} rotate so that every step reads cold HBM
-(the copies together are at least twice the 256 MB Infinity Cache).  The K
-timed steps are captured once in a HIP graph and replayed, so the host's
-launch cost does not starve the GPU; HIP events bracket the replay on the
-stream the kernels run on.
+Default (no --workload): ONE JSON line.  Its `value` is the decode gate+up
+GEMV (M=1, K=7168, N=4096: effective HBM GB/s of w4a16_gemm), and its
+`configs` object holds every workload the metric names, each timed the same
+way through the entry point w4a16_gemm runs (auto path):
 
-One JSON line is printed per workload (by default only the decode gate+up
-GEMV, M=1 K=7168 N=4096, which the headline metric is quoted on).
+  tiny (1x256x512), decode_gate_up (1x7168x4096), decode_down (1x2048x7168),
+  verify_tree (64x7168x4096), prefill (4096x7168x4096)
+
+with ms per step, GB/s, TFLOP/s, the kernel path and arithmetic, the fraction
+of the roof that binds it (HBM when the FLOPs are under the ridge of the
+path's arithmetic, otherwise that arithmetic's matrix peak), the
+streaming-read floor of the same bytes (a plain read of X, qweight and scales
+over the same rotating buffers, `w4a16_read_floor`, best of six launch
+shapes), the fp32-FMA GEMV beside the matrix-core GEMV for the M=1 decodes,
+and the other entry points for the two larger shapes (repacked, small-packed,
+split on packed weights; their one-time repack is timed apart).
+
+With --workload, one JSON line per (workload, path) instead (for profiling):
+paths auto, gemv, gemv-fma, tile, split, packed, swiglu, repacked,
+small-packed, read-floor (the plain read of the same inputs, 256 threads x 4
+loads); grouped-MoE workloads take the public layout, or `packed` for the
+repacked grouped weights.
+
+A step is one call of the entry point (validate, launch, unpack + dequant +
+contraction + reduction + store) on one batch of synthetic input, with inputs
+already resident in HBM.  Every timed step reads its own copy of {X, qweight,
+scales} (no copy is read twice in the timed steps, and the copies together
+hold at least 512 MB, twice the 256 MB Infinity Cache), and 1 GiB is streamed
+through the caches right before the timed steps, so every timed step reads
+cold HBM.  The K steps are captured once in a HIP graph and replayed between
+HIP events on the stream the kernels run on; ms_per_step is the replay time /
+K.  A bounded spin kernel runs just before the start event, so that the host's
+submission of the replay is not counted as GPU time.  Eager per-launch event
+times (median, p10, p90) are reported beside it.
 """
 
 from __future__ import annotations
@@ -34,6 +47,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -49,21 +63,28 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published
 MALL_BYTES = 256 << 20
+ROTATION_MIN_BYTES = 2 * MALL_BYTES
+ROTATION_MAX_BYTES = 16 << 30
+FLUSH_BYTES = 1 << 30
+SPIN_CYCLES = 1_000_000      # GPU clock cycles of the spin before the timed region
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "int4_weight_only_03_amd/csrc/"
-PATH_NAMES = {"auto": 0, "gemv": 1, "tile": 2, "split": 3, "packed": 4, "swiglu": 5,
-              "repacked": 6, "small-packed": 7}
-SPLIT_PATHS = ("split", "packed")
+PATHS = ("auto", "gemv", "gemv-fma", "tile", "split", "packed", "swiglu", "repacked",
+         "small-packed", "read-floor")
 # paths whose products are fp16 matrix instructions on two activation limbs
 LIMB_PATHS = ("split", "packed", "repacked", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
-PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"], "tile": ["tile.hip"],
+PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
+                "gemv-fma": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "repacked": ["packed_gemv.hip", "small_packed.hip", "gemv_common.h", "limbs.h"],
-                "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"]}
+                "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"],
+                "read-floor": ["read_floor.hip", "gemv_common.h"]}
+# launch shapes of the streaming-read floor: (threads per block, 16-byte loads per thread)
+FLOOR_SHAPES = [(256, 1), (256, 4), (1024, 4), (512, 8), (256, 16), (1024, 16)]
 
 
 def source_hash(path: str) -> str:
@@ -87,16 +108,30 @@ def measured_traffic(workload: str, path: str):
     return entry.get("bytes_per_launch")
 
 
-def metric_in_gbs(wl) -> bool:
+def metric_in_gbs(M: int) -> bool:
     """The metric is effective HBM GB/s for M <= 64 and TFLOP/s above."""
-    return wl.M <= 64
+    return M <= 64
+
+
+_FLUSH = None
+
+
+def flush_caches():
+    """Stream 1 GiB (read and write) through L2 and the Infinity Cache."""
+    import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    _FLUSH.add_(1.0)
 
 
 def time_steps(step, steps: int, stream):
-    """(ms per step of a graph replay of `steps` steps, eager per-launch ms, graphed)."""
+    """(ms per step of a graph replay of `steps` steps, eager per-launch ms, graphed).
+
+    Eager launches with events around each give per-launch times; then the
+    steps are captured in a graph, replayed once to warm up, the caches are
+    flushed, and the timed replay runs between two events on `stream`."""
     import torch
-    # per-launch durations with events around each launch (eager), for the
-    # kernel-time cross-check against rocprofv3
     n_ev = min(steps, 200)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
@@ -119,9 +154,14 @@ def time_steps(step, steps: int, stream):
         graphed = False
         print(f"# graph capture failed ({e}); timing eager launches", file=sys.stderr)
 
+    flush_caches()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # a bounded spin kernel keeps the GPU busy while the host submits the
+    # replay, so the host's submission latency falls before the start event
+    # and the events bracket only the K steps' GPU work
+    torch.cuda._sleep(SPIN_CYCLES)
     start.record(stream)
     if graphed:
         g.replay()
@@ -131,6 +171,397 @@ def time_steps(step, steps: int, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps, per_launch_ms, graphed
+
+
+def timing_fields(ms, per_launch_ms, graphed):
+    return {"ms_per_step": ms, "us_per_step": ms * 1e3, "graph_replay": graphed,
+            "per_launch_event_us_median": statistics.median(per_launch_ms) * 1e3,
+            "per_launch_event_us_p10": float(np.percentile(per_launch_ms, 10)) * 1e3,
+            "per_launch_event_us_p90": float(np.percentile(per_launch_ms, 90)) * 1e3}
+
+
+class Problem:
+    """One workload's inputs, quantized by the library's host quantizer, in
+    rotating device copies (each timed step reads its own copy)."""
+
+    def __init__(self, name: str, steps: int):
+        import torch
+        import int4_weight_only_03_amd as pkg
+        self.pkg = pkg
+        self.name = name
+        self.wl = wl = workloads.WORKLOADS[name]
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.X, self.W = workloads.make(name)
+        self.qw, self.sc = pkg.w4a16_quantize(self.W)
+        self.B = wl.algorithmic_bytes()
+        self.flops = wl.flops()
+        if name == "tiny":
+            copies = 1                                # cache-resident by nature
+        else:
+            copies = max(-(-ROTATION_MIN_BYTES // self.B), steps)
+            copies = max(1, min(copies, ROTATION_MAX_BYTES // self.B))
+        self.copies = copies
+        Xd = torch.from_numpy(self.X).to(self.dev)
+        Qd = torch.from_numpy(self.qw).to(self.dev)
+        Sd = torch.from_numpy(self.sc).to(self.dev)
+        self.sets = [(Xd.clone(), Qd.clone(), Sd.clone(),
+                      torch.empty((wl.M, wl.N), dtype=torch.float32, device=self.dev))
+                     for _ in range(copies)]
+        del Xd, Qd, Sd
+        torch.cuda.synchronize()
+
+    def input_sha256(self):
+        return {"X": workloads.sha256(self.X)[:16], "W": workloads.sha256(self.W)[:16]}
+
+    def _repack(self, fn):
+        """fn(q, s) -> packed for every copy; returns (packs, ms of one repack)."""
+        import torch
+        packs = [fn(q, s) for (_, q, s, _) in self.sets]
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        fn(self.sets[0][1], self.sets[0][2])
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return packs, a.elapsed_time(b)
+
+    def measure(self, path: str, steps: int, warmup: int) -> dict:
+        """Time `steps` steps of one entry point; returns timing, rates and Y of copy 0."""
+        import torch
+        pkg, wl, sets, C = self.pkg, self.wl, self.sets, self.copies
+        B = self.B
+        repack_ms = None
+        y_out = [s[3] for s in sets]
+        if path in ("split", "packed"):
+            ws = torch.empty(pkg.w4a16_split_workspace_bytes(wl.M, wl.N, wl.K),
+                             dtype=torch.uint8, device=self.dev)
+        if path == "split":
+            def step(i):
+                x, q, s, y = sets[i % C]
+                pkg.w4a16_gemm_split(x, q, s, y, workspace=ws)
+        elif path == "packed":
+            packs, repack_ms = self._repack(lambda q, s: pkg.w4a16_split_pack(q, s))
+
+            def step(i):
+                x, _, _, y = sets[i % C]
+                pkg.w4a16_gemm_split_packed(x, packs[i % C], wl.N, y, workspace=ws)
+        elif path == "repacked":
+            packs, repack_ms = self._repack(lambda q, s: pkg.w4a16_repack(q, s))
+
+            def step(i):
+                x, _, _, y = sets[i % C]
+                pkg.w4a16_gemm_repacked(x, packs[i % C], wl.N, y)
+        elif path == "small-packed":
+            packs, repack_ms = self._repack(lambda q, s: pkg.w4a16_grouped_pack(q[None], s[None]))
+            need = pkg.w4a16_small_packed_workspace_bytes(wl.M, wl.N, wl.K)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.dev)
+
+            def step(i):
+                x, _, _, y = sets[i % C]
+                pkg.w4a16_gemm_small_packed(x, packs[i % C], wl.N, y, workspace=ws)
+        elif path == "read-floor":
+            # the streaming read of the same X, qweight and scales (256 threads x 4 loads)
+            sink = torch.zeros(4, dtype=torch.int32, device=self.dev)
+            B -= 4 * wl.M * wl.N
+
+            def step(i):
+                x, q, s, _ = sets[i % C]
+                pkg.w4a16_read_floor([x, q, s], sink, 256, 4)
+        elif path == "swiglu":
+            B -= 4 * wl.M * (wl.N // 2)   # Y is [M][N/2]: the gate/up outputs never reach memory
+            y_out = [torch.empty((wl.M, wl.N // 2), dtype=torch.float32, device=self.dev)
+                     for _ in range(C)]
+
+            def step(i):
+                x, q, s, _ = sets[i % C]
+                pkg.w4a16_gemm_swiglu(x, q, s, y_out[i % C])
+        else:
+            code = {"auto": pkg.W4A16_PATH_AUTO, "gemv": pkg.W4A16_PATH_GEMV,
+                    "gemv-fma": pkg.W4A16_PATH_GEMV_FMA, "tile": pkg.W4A16_PATH_TILE}[path]
+
+            def step(i):
+                x, q, s, y = sets[i % C]
+                pkg.w4a16_gemm_path(x, q, s, y, path=code)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ms, per_launch_ms, graphed = time_steps(step, steps, self.stream)
+        resolved = self.resolve(path)
+        limb = self.limb(resolved)
+        gbs = B / (ms * 1e-3) / 1e9
+        tfs = self.flops / (ms * 1e-3) / 1e12
+        peak_tf = FP16_PEAK_TFLOPS if limb else FP32_PEAK_TFLOPS
+        if self.flops / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
+            roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS}
+        else:
+            roof = {"bound": "mfma", "achieved": tfs, "peak": peak_tf, "unit": "TFLOP/s",
+                    "frac": tfs / peak_tf}
+        roof["traffic"] = measured_traffic(self.name, resolved)
+        out = {"path": resolved, "dtype": "f16x2-limb/f32-acc" if limb else "f32",
+               "algorithmic_bytes": B, "flops": self.flops, "GB_s": gbs, "TFLOP_s": tfs,
+               "hbm_frac": gbs / HBM_PEAK_GBS, "fp32_frac": tfs / FP32_PEAK_TFLOPS,
+               "roofline": roof, "repack_ms_one_time": repack_ms,
+               "rotation_copies": self.copies,
+               "timed_set_bytes": min(steps, self.copies) * B}
+        out.update(timing_fields(ms, per_launch_ms, graphed))
+        torch.cuda.synchronize()
+        out["_y0"] = y_out[0].cpu().numpy()
+        return out
+
+    def resolve(self, path: str) -> str:
+        if path != "auto":
+            return path
+        code = self.pkg.w4a16_select_path(self.wl.M, self.wl.N, self.wl.K)
+        return "gemv" if code == self.pkg.W4A16_PATH_GEMV else "tile"
+
+    def limb(self, resolved: str) -> bool:
+        """Whether the path's products are fp16 matrix instructions on activation limbs."""
+        wl = self.wl
+        return resolved in LIMB_PATHS or (
+            resolved in ("gemv", "swiglu")
+            and self.pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == self.pkg.W4A16_GEMV_MFMA)
+
+    def read_floor(self, steps: int, warmup: int) -> dict:
+        """Best plain streaming read of the same X, qweight and scales buffers."""
+        import torch
+        sink = torch.zeros(4, dtype=torch.int32, device=self.dev)
+        Bread = sum(t.numel() * t.element_size() for t in self.sets[0][:3])
+        best, shapes = None, {}
+        for threads, loads in FLOOR_SHAPES:
+            def step(i, threads=threads, loads=loads):
+                x, q, s, _ = self.sets[i % self.copies]
+                self.pkg.w4a16_read_floor([x, q, s], sink, threads, loads)
+            for i in range(warmup):
+                step(i)
+            ms, _, _ = time_steps(step, steps, self.stream)
+            shapes[f"{threads}x{loads}"] = ms * 1e3
+            if best is None or ms < best[0]:
+                best = (ms, threads, loads)
+        ms, threads, loads = best
+        return {"read_floor_us": ms * 1e3, "read_floor_bytes": Bread,
+                "read_floor_GB_s": Bread / (ms * 1e-3) / 1e9,
+                "read_floor_hbm_frac": Bread / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "read_floor_shape": f"{threads} threads x {loads} loads",
+                "read_floor_us_by_shape": shapes}
+
+
+def steps_for(M: int, steps: int) -> int:
+    return steps if M < 1024 else max(5, min(steps, 20))
+
+
+def cpu_facts() -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:                                 # pragma: no cover
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def cpu_leg(outputs: dict, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, timed on the host cores: a bounded sample of
+    the headline workload (value), one full run of the prefill oracle, and the
+    GPU parity of copy 0 of every timed workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                               # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        # the headline sample: decode_gate_up, its one row against all weight rows
+        wl = workloads.WORKLOADS["decode_gate_up"]
+        X, W = workloads.make("decode_gate_up")
+        qw, sc = oracle.quantize(W)
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or not times:
+            t0 = time.perf_counter()
+            oracle.gemm(X, qw, sc)                    # dequant + fp64 product
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 50:
+                break
+        t = statistics.median(times)
+        value = wl.algorithmic_bytes() / t / 1e9
+        res = {"value": value, "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"decode_gate_up whole (1 row of X against all {wl.N} weight rows: "
+                         f"dequant + fp64 product), median of {len(times)} runs, "
+                         f"{t * 1e3:.1f} ms each"}
+        res.update(cpu_facts())
+        # parity of every timed workload (one copy each), and one prefill oracle run
+        parity = {}
+        for name, y in outputs.items():
+            Xn, Wn = workloads.make(name)
+            qn, sn = oracle.quantize(Wn)
+            t0 = time.perf_counter()
+            Yref = oracle.gemm(Xn, qn, sn)
+            dt = time.perf_counter() - t0
+            T = oracle.abs_gemm(Xn, qn, sn)
+            parity[name] = oracle.compare_to(y, Yref, T)["max_ratio"]
+            if name == "prefill":
+                wlp = workloads.WORKLOADS["prefill"]
+                res["prefill_oracle_s_one_rep"] = dt
+                res["prefill_oracle_TFLOP_s"] = wlp.flops() / dt / 1e12
+        res["gpu_parity_max_err_over_bound"] = parity
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return res
+
+
+def gpu_clocks():
+    """Current shader and memory clocks (rocm-smi), if it is there."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = next(iter(d.values()))
+        return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k or "fclk" in k}
+    except Exception:
+        return None
+
+
+def headline(args) -> None:
+    """Every configuration of the metric in one line; value = decode_gate_up."""
+    import torch
+    configs, outputs = {}, {}
+    for name in workloads.ORDER:
+        wl = workloads.WORKLOADS[name]
+        steps = steps_for(wl.M, args.steps)
+        print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps}", file=sys.stderr, flush=True)
+        prob = Problem(name, steps)
+        r = prob.measure("auto", steps, args.warmup)
+        outputs[name] = r.pop("_y0")
+        r.update(prob.read_floor(steps, args.warmup))
+        r["us_over_read_floor"] = r["us_per_step"] / r["read_floor_us"]
+        r["config"] = {"M": wl.M, "K": wl.K, "N": wl.N, "note": wl.note}
+        r["input_sha256"] = prob.input_sha256()
+        r["steps"] = steps
+        if name in ("decode_gate_up", "decode_down"):
+            f = prob.measure("gemv-fma", steps, args.warmup)
+            f.pop("_y0")
+            r["fp32_fma_gemv"] = {k: f[k] for k in ("us_per_step", "GB_s", "hbm_frac", "dtype",
+                                                   "per_launch_event_us_median")}
+        if name in ("verify_tree", "prefill"):
+            alts = {}
+            others = ("small-packed", "repacked", "packed") if wl.M <= 64 else ("packed",
+                                                                                "repacked")
+            for p in others:
+                a = prob.measure(p, steps, args.warmup)
+                a.pop("_y0")
+                alts[p] = {k: a[k] for k in ("us_per_step", "GB_s", "TFLOP_s", "hbm_frac",
+                                             "fp32_frac", "dtype", "repack_ms_one_time")}
+                alts[p]["frac_of_fp16_peak"] = a["TFLOP_s"] / FP16_PEAK_TFLOPS
+            r["other_entry_points"] = alts
+        configs[name] = r
+        del prob
+        torch.cuda.empty_cache()
+
+    head = configs["decode_gate_up"]
+    line = {
+        "metric": METRIC, "value": head["GB_s"], "unit": "GB/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic",
+        "config": {"workload": "decode_gate_up", "M": 1, "K": 7168, "N": 4096, "group": 32,
+                   "note": workloads.WORKLOADS["decode_gate_up"].note,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "path": head["path"],
+        "read_floor_us": head["read_floor_us"],
+        "configs": configs,
+        "gpu_clocks": gpu_clocks(),
+        "rotation": "each timed step reads its own copy of X, qweight and scales; 1 GiB "
+                    "streamed through the caches before the timed steps",
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_leg(outputs)
+    print(json.dumps(line), flush=True)
+
+
+def per_path(args) -> None:
+    names = (workloads.ORDER + list(workloads.MOE_WORKLOADS) if args.workload == "all"
+             else args.workload.split(","))
+    paths = args.path.split(",")
+    for p in paths:
+        if p not in PATHS:
+            raise SystemExit(f"unknown path {p!r}")
+    for name in names:
+        if name in workloads.MOE_WORKLOADS:
+            if any(p != "packed" for p in paths):
+                run_moe(name, args)
+            if "packed" in paths:
+                run_moe(name, args, packed=True)
+            continue
+        wl = workloads.WORKLOADS[name]
+        steps = steps_for(wl.M, args.steps)
+        prob = Problem(name, steps)
+        for path in paths:
+            print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps} path={path}",
+                  file=sys.stderr, flush=True)
+            r = prob.measure(path, steps, args.warmup)
+            y0 = r.pop("_y0")
+            metric_gbs = metric_in_gbs(wl.M)
+            line = {
+                "metric": METRIC, "value": r["GB_s"] if metric_gbs else r["TFLOP_s"],
+                "unit": "GB/s" if metric_gbs else "TFLOP/s", "n_gpus": 1, "steps": steps,
+                "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": r["dtype"], "data": "synthetic",
+                "config": {"workload": name, "M": wl.M, "K": wl.K, "N": wl.N, "group": 32,
+                           "note": wl.note, "parallelism": "none (1 GPU)"},
+                "roofline": r.pop("roofline"),
+            }
+            line.update(r)
+            if not args.no_cpu:
+                line["cpu_baseline"] = cpu_leg_sample(name, y0, path)
+            print(json.dumps(line), flush=True)
+        del prob
+
+
+def cpu_leg_sample(name: str, Y, path: str, budget_s: float = 12.0) -> dict:
+    """The oracle on up to 8 rows of one workload (per-path lines)."""
+    import oracle
+    wl = workloads.WORKLOADS[name]
+    X, W = workloads.make(name)
+    qw, sc = oracle.quantize(W)
+    rows = min(wl.M, 8)
+    Xs = np.ascontiguousarray(X[:rows])
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        Yref = oracle.swiglu(Xs, qw, sc) if path == "swiglu" else oracle.gemm(Xs, qw, sc)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    t = statistics.median(times)
+    sample_bytes = wl.N * wl.K // 2 + 4 * wl.N * (wl.K // 32) + 4 * rows * (wl.K + wl.N)
+    if path == "swiglu":
+        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.swiglu_bound(Xs, qw, sc)
+    else:
+        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.bound(
+            oracle.abs_gemm(Xs, qw, sc))
+    return {"value": sample_bytes / t / 1e9, "unit": "GB/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of X against all {wl.N} weight rows, median of "
+                      f"{len(times)} runs, {t * 1e3:.1f} ms each",
+            "gpu_parity_on_sample_max_err_over_bound": float(err.max())}
 
 
 def gpu_leg_moe(name: str, steps: int, warmup: int, packed: bool = False):
@@ -147,7 +578,8 @@ def gpu_leg_moe(name: str, steps: int, warmup: int, packed: bool = False):
     sc = np.stack([s for _, s in quantized])
     del quantized
     B = wl.algorithmic_bytes(off)
-    copies = max(1, -(-2 * MALL_BYTES // B))
+    copies = max(-(-ROTATION_MIN_BYTES // B), steps)
+    copies = max(1, min(copies, ROTATION_MAX_BYTES // B))
     Xd, Qd, Sd = (torch.from_numpy(a).to(dev) for a in (X, qw, sc))
     Id, Od = torch.from_numpy(ti).to(dev), torch.from_numpy(off).to(dev)
     sets = [(Xd.clone(), Qd.clone(), Sd.clone(),
@@ -176,23 +608,21 @@ def gpu_leg_moe(name: str, steps: int, warmup: int, packed: bool = False):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ms_per_step, per_launch_ms, graphed = time_steps(step, steps, stream)
-    gbs = B / (ms_per_step * 1e-3) / 1e9
-    tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
+    ms, per_launch_ms, graphed = time_steps(step, steps, stream)
+    gbs = B / (ms * 1e-3) / 1e9
+    tfs = wl.flops() / (ms * 1e-3) / 1e12
     path = "grouped-packed" if packed else "grouped"
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name, path)}
-    med = statistics.median(per_launch_ms)
     active = int(np.count_nonzero(np.diff(off)))
-    extra = {"graph_replay": graphed, "rotation_copies": copies, "algorithmic_bytes": B,
-             "flops": wl.flops(), "per_launch_event_us_median": med * 1e3,
-             "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9, "path": path,
-             "active_experts": active, "hbm_frac": gbs / HBM_PEAK_GBS,
+    extra = {"rotation_copies": copies, "algorithmic_bytes": B, "flops": wl.flops(),
+             "path": path, "active_experts": active, "hbm_frac": gbs / HBM_PEAK_GBS,
              "fp32_frac": tfs / FP32_PEAK_TFLOPS}
+    extra.update(timing_fields(ms, per_launch_ms, graphed))
     if repack_ms is not None:
         extra["repack_ms_one_time"] = repack_ms
     y0 = sets[0][3].cpu().numpy()
-    return gbs, "GB/s", ms_per_step, roof, extra, (X, qw, sc, ti, off, y0)
+    return gbs, ms, roof, extra, (X, qw, sc, ti, off, y0)
 
 
 def cpu_leg_moe(name: str, gpu_out, budget_s: float = 12.0):
@@ -201,17 +631,16 @@ def cpu_leg_moe(name: str, gpu_out, budget_s: float = 12.0):
     wl = workloads.MOE_WORKLOADS[name]
     X, qw, sc, ti, off, Y = gpu_out
     cores = len(os.sched_getaffinity(0))
-    # sample: every slot of the first experts, up to 8 slots
     e_end = 1
     while e_end < wl.E and off[e_end + 1] <= 8:
         e_end += 1
     r_end = int(off[e_end])
     sub_off = off[:e_end + 1]
-    times, Yref = [], None
+    times = []
     t_end = time.perf_counter() + budget_s
     while time.perf_counter() < t_end or not times:
         t0 = time.perf_counter()
-        Yref = oracle.grouped_gemm(X, ti[:r_end], sub_off, qw[:e_end], sc[:e_end])
+        oracle.grouped_gemm(X, ti[:r_end], sub_off, qw[:e_end], sc[:e_end])
         times.append(time.perf_counter() - t0)
         if len(times) >= 50:
             break
@@ -225,190 +654,30 @@ def cpu_leg_moe(name: str, gpu_out, budget_s: float = 12.0):
             "gpu_parity_on_sample_max_err_over_bound": v["max_ratio"]}
 
 
-def gpu_leg(name: str, steps: int, warmup: int, path: str = "auto"):
-    import torch
-    import int4_weight_only_03_amd as pkg
+def moe_dtype(wl) -> str:
+    """Arithmetic of the grouped kernel the library picks for this workload."""
+    from int4_weight_only_03_amd import binding
+    k = binding.w4a16_grouped_kernel(wl.T, wl.R, wl.E, wl.N, wl.K)
+    return "f16x2-limb/f32-acc" if k == binding.W4A16_GROUPED_MFMA else "f32"
 
-    wl = workloads.WORKLOADS[name]
-    dev = torch.device("cuda:0")
-    X, W = workloads.make(name)
-    qw, sc = pkg.w4a16_quantize(W)            # the library's own host quantizer
-    B = wl.algorithmic_bytes()
-    if path == "swiglu":  # Y is [M][N/2]: the gate/up outputs never reach memory
-        B -= 4 * wl.M * (wl.N // 2)
-    copies = 1 if B * 2 > 4 * MALL_BYTES else max(1, -(-2 * MALL_BYTES // B))
-    if name == "tiny":
-        copies = 1                             # cache-resident by nature
-    Xd = torch.from_numpy(X).to(dev)
-    Qd = torch.from_numpy(qw).to(dev)
-    Sd = torch.from_numpy(sc).to(dev)
-    sets = [(Xd.clone(), Qd.clone(), Sd.clone(),
-             torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)) for _ in range(copies)]
-    del Xd, Qd, Sd
-    stream = torch.cuda.current_stream(dev)
-    code = PATH_NAMES[path]
-    repack_ms = None
-    if path in SPLIT_PATHS:
-        # one caller-owned workspace, reused by every (stream-ordered) step
-        ws = torch.empty(pkg.w4a16_split_workspace_bytes(wl.M, wl.N, wl.K), dtype=torch.uint8,
-                         device=dev)
-    if path == "split":
-        def step(i):
-            x, q, s, y = sets[i % copies]
-            pkg.w4a16_gemm_split(x, q, s, y, workspace=ws)
-    elif path == "packed":
-        # the one-time repack (outside the timed region, timed on its own)
-        packs = [pkg.w4a16_split_pack(q, s) for (_, q, s, _) in sets]
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        pkg.w4a16_split_pack(sets[0][1], sets[0][2], packs[0])
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        repack_ms = ev0.elapsed_time(ev1)
 
-        def step(i):
-            x, _, _, y = sets[i % copies]
-            pkg.w4a16_gemm_split_packed(x, packs[i % copies], wl.N, y, workspace=ws)
-    elif path == "repacked":
-        # the one-time repack (w4a16_repack), timed on its own
-        packs = [pkg.w4a16_repack(q, s) for (_, q, s, _) in sets]
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        pkg.w4a16_repack(sets[0][1], sets[0][2], packs[0])
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        repack_ms = ev0.elapsed_time(ev1)
-
-        def step(i):
-            x, _, _, y = sets[i % copies]
-            pkg.w4a16_gemm_repacked(x, packs[i % copies], wl.N, y)
-    elif path == "small-packed":
-        # the one-time repack into the grouped layout (one expert), timed on its own
-        packs = [pkg.w4a16_grouped_pack(q[None], s[None]) for (_, q, s, _) in sets]
-        need = pkg.w4a16_small_packed_workspace_bytes(wl.M, wl.N, wl.K)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        pkg.w4a16_grouped_pack(sets[0][1][None], sets[0][2][None], packs[0])
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        repack_ms = ev0.elapsed_time(ev1)
-
-        def step(i):
-            x, _, _, y = sets[i % copies]
-            pkg.w4a16_gemm_small_packed(x, packs[i % copies], wl.N, y, workspace=ws)
-    elif path == "swiglu":
-        ys = [torch.empty((wl.M, wl.N // 2), dtype=torch.float32, device=dev)
-              for _ in range(copies)]
-
-        def step(i):
-            x, q, s, _ = sets[i % copies]
-            pkg.w4a16_gemm_swiglu(x, q, s, ys[i % copies])
-    else:
-        def step(i):
-            x, q, s, y = sets[i % copies]
-            pkg.w4a16_gemm_path(x, q, s, y, path=code)
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    ms_per_step, per_launch_ms, graphed = time_steps(step, steps, stream)
-
-    gbs = B / (ms_per_step * 1e-3) / 1e9
-    tfs = wl.flops() / (ms_per_step * 1e-3) / 1e12
-    value, unit = (gbs, "GB/s") if metric_in_gbs(wl) else (tfs, "TFLOP/s")
-    resolved = path if path != "auto" else \
-        {1: "gemv", 2: "tile"}[pkg.w4a16_select_path(wl.M, wl.N, wl.K)]
-    # the limb paths issue fp16 matrix instructions (so does the GEMV path's
-    # matrix-core kernel): their compute roof is the fp16 peak
-    split = path in LIMB_PATHS or (
-        resolved in ("gemv", "swiglu")
-        and pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == pkg.W4A16_GEMV_MFMA)
-    peak_tf = FP16_PEAK_TFLOPS if split else FP32_PEAK_TFLOPS
-    if wl.flops() / (peak_tf * 1e12) < B / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS}
-    else:
-        roof = {"bound": "mfma", "achieved": tfs, "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": tfs / peak_tf}
-    roof["traffic"] = measured_traffic(name, resolved)
-    med = statistics.median(per_launch_ms)
-    extra = {
-        "graph_replay": graphed,
-        "rotation_copies": copies,
-        "algorithmic_bytes": B,
-        "flops": wl.flops(),
-        "per_launch_event_us_median": med * 1e3,
-        "per_launch_event_us_p10": float(np.percentile(per_launch_ms, 10)) * 1e3,
-        "per_launch_event_us_p90": float(np.percentile(per_launch_ms, 90)) * 1e3,
-        "hbm_GBs_at_event_median": B / (med * 1e-3) / 1e9,
-        "tflops_at_event_median": wl.flops() / (med * 1e-3) / 1e12,
-        "path": resolved,
-        "hbm_frac": gbs / HBM_PEAK_GBS,
-        "repack_ms_one_time": repack_ms,
-        "fp32_frac": tfs / FP32_PEAK_TFLOPS,
-        "limb_arithmetic": split,
+def run_moe(name, args, packed=False):
+    wl = workloads.MOE_WORKLOADS[name]
+    print(f"# {name}: T={wl.T} E={wl.E} top-{wl.topk} K={wl.K} N={wl.N} steps={args.steps} "
+          f"path={'grouped-packed' if packed else 'grouped'}", file=sys.stderr, flush=True)
+    value, ms, roof, extra, out = gpu_leg_moe(name, args.steps, args.warmup, packed)
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": moe_dtype(wl), "data": "synthetic",
+        "config": {"workload": name, "T": wl.T, "experts": wl.E, "topk": wl.topk, "K": wl.K,
+                   "N": wl.N, "group": 32, "note": wl.note, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
     }
-    y0 = (ys[0] if path == "swiglu" else sets[0][3]).cpu().numpy()
-    return value, unit, ms_per_step, roof, extra, (X, W, y0)
-
-
-def cpu_leg(name: str, gpu_out, budget_s: float = 12.0, path: str = "auto"):
-    """The oracle, as it stands, timed on the host cores over a bounded sample."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:                               # pragma: no cover
-        threadpool_limits = None
-    wl = workloads.WORKLOADS[name]
-    X, W, Y = gpu_out
-    cores = len(os.sched_getaffinity(0))
-    qw, sc = oracle.quantize(W)
-    # sample: all N outputs of up to 8 rows of X (the whole job when M <= 8)
-    rows = min(wl.M, 8)
-    Xs = np.ascontiguousarray(X[:rows])
-    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        times = []
-        t_end = time.perf_counter() + budget_s
-        Yref = None
-        while time.perf_counter() < t_end or not times:
-            t0 = time.perf_counter()
-            if path == "swiglu":
-                Yref = oracle.swiglu(Xs, qw, sc)      # dequant + fp64 product + epilogue
-            else:
-                Yref = oracle.gemm(Xs, qw, sc)        # dequant + fp64 product
-            times.append(time.perf_counter() - t0)
-            if len(times) >= 50:
-                break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    t = statistics.median(times)
-    # the sample's share of the workload's algorithmic bytes / flops
-    sample_bytes = wl.N * wl.K // 2 + 4 * wl.N * (wl.K // 32) + 4 * rows * wl.K + 4 * rows * wl.N
-    sample_flops = 2 * rows * wl.N * wl.K
-    if metric_in_gbs(wl):
-        value, unit = sample_bytes / t / 1e9, "GB/s"
-    else:
-        value, unit = sample_flops / t / 1e12, "TFLOP/s"
-    if path == "swiglu":
-        sample_bytes -= 4 * rows * (wl.N // 2)
-        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.swiglu_bound(Xs, qw, sc)
-    else:
-        T = oracle.abs_gemm(Xs, qw, sc)
-        err = np.abs(Y[:rows].astype(np.float64) - Yref) / oracle.bound(T)
-    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of X against all {wl.N} weight rows "
-                      f"(dequant + fp64 product), median of {len(times)} runs, "
-                      f"{t * 1e3:.1f} ms each",
-            "gpu_parity_on_sample_max_err_over_bound": float(err.max())}
+    line.update(extra)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_leg_moe(name, out)
+    print(json.dumps(line), flush=True)
 
 
 def copy_probe(nbytes: int, reps: int = 20) -> None:
@@ -429,13 +698,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_gate_up",
-                    help="comma-separated names from %s, or 'all'" % ", ".join(
-                        workloads.ORDER + list(workloads.MOE_WORKLOADS)))
-    ap.add_argument("--path", default="auto",
-                    help="kernel path(s), comma-separated: auto, gemv, tile, split, packed, "
-                         "swiglu, repacked, small-packed; grouped-MoE workloads run the grouped kernel on the "
-                         "public layout, or with 'packed' on the repacked weights")
+    ap.add_argument("--workload", default=None,
+                    help="comma-separated names from %s, or 'all' (one line per workload "
+                         "and path instead of the headline line)" % ", ".join(
+                             workloads.ORDER + list(workloads.MOE_WORKLOADS)))
+    ap.add_argument("--path", default="auto", help="with --workload: " + ", ".join(PATHS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -447,67 +714,10 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    names = (workloads.ORDER + list(workloads.MOE_WORKLOADS) if args.workload == "all"
-             else args.workload.split(","))
-    paths = args.path.split(",")
-    for p in paths:
-        if p not in PATH_NAMES:
-            ap.error(f"unknown path {p!r}")
-    for name in names:
-        if name in workloads.MOE_WORKLOADS:
-            # "packed": the repacked grouped weights; any other path: the public layout
-            if any(p != "packed" for p in paths):
-                run_moe(name, args)
-            if "packed" in paths:
-                run_moe(name, args, packed=True)
-    names = [n for n in names if n not in workloads.MOE_WORKLOADS]
-    for name, path in [(n, p) for n in names for p in paths]:
-        wl = workloads.WORKLOADS[name]
-        steps = args.steps if wl.M < 1024 else max(5, min(args.steps, 20))
-        print(f"# {name}: M={wl.M} K={wl.K} N={wl.N} steps={steps} path={path}",
-              file=sys.stderr, flush=True)
-        value, unit, ms, roof, extra, out = gpu_leg(name, steps, args.warmup, path)
-        # arithmetic type: fp32 FMA/MFMA, or fp16 matrix products of two fp16
-        # activation limbs and exact weight codes with fp32 accumulation
-        dtype = "f16x2-limb/f32-acc" if extra["limb_arithmetic"] else "f32"
-        line = {
-            "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
-            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-            "config": {"workload": name, "M": wl.M, "K": wl.K, "N": wl.N, "group": 32,
-                       "note": wl.note, "parallelism": "none (1 GPU)"},
-            "roofline": roof,
-        }
-        line.update(extra)
-        if not args.no_cpu:
-            line["cpu_baseline"] = cpu_leg(name, out, path=path)
-        print(json.dumps(line), flush=True)
-
-
-def moe_dtype(wl) -> str:
-    """Arithmetic of the grouped kernel the library picks for this workload."""
-    from int4_weight_only_03_amd import binding
-    k = binding.w4a16_grouped_kernel(wl.T, wl.R, wl.E, wl.N, wl.K)
-    return "f16x2-limb/f32-acc" if k == binding.W4A16_GROUPED_MFMA else "f32"
-
-
-def run_moe(name, args, packed=False):
-    wl = workloads.MOE_WORKLOADS[name]
-    print(f"# {name}: T={wl.T} E={wl.E} top-{wl.topk} K={wl.K} N={wl.N} steps={args.steps} "
-          f"path={'grouped-packed' if packed else 'grouped'}", file=sys.stderr, flush=True)
-    value, unit, ms, roof, extra, out = gpu_leg_moe(name, args.steps, args.warmup, packed)
-    line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": moe_dtype(wl), "data": "synthetic",
-        "config": {"workload": name, "T": wl.T, "experts": wl.E, "topk": wl.topk, "K": wl.K,
-                   "N": wl.N, "group": 32, "note": wl.note, "parallelism": "none (1 GPU)"},
-        "roofline": roof,
-    }
-    line.update(extra)
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_leg_moe(name, out)
-    print(json.dumps(line), flush=True)
+    if args.workload is None:
+        headline(args)
+    else:
+        per_path(args)
 
 
 if __name__ == "__main__":

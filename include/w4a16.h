@@ -82,6 +82,9 @@ extern "C" {
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
 #define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
                                  exact (q - 8) codes and two fp16 limbs of each activation */
+#define W4A16_PATH_GEMV_FMA 4 /* the fp32 FMA GEMV kernels for any M and K: one fp32 FMA per
+                                 weight with the activations in VGPRs (the GEMV path's kernel
+                                 for K > 8192); for measurement beside the matrix-core GEMV */
 
 /* Version of this ABI (W4A16_ABI_VERSION of the library that was built). */
 int w4a16_abi_version(void);
@@ -112,9 +115,9 @@ int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, floa
                int64_t M, int64_t N, int64_t K, int32_t group, void *stream);
 
 /*
- * As w4a16_gemm, but with the kernel path forced (W4A16_PATH_AUTO, _GEMV or
- * _TILE; W4A16_PATH_SPLIT needs a workspace and is refused here with
- * W4A16_ERR_ARG).  Every path accepts every valid shape.  For tests and
+ * As w4a16_gemm, but with the kernel path forced (W4A16_PATH_AUTO, _GEMV,
+ * _TILE or _GEMV_FMA; W4A16_PATH_SPLIT needs a workspace and is refused here
+ * with W4A16_ERR_ARG).  Every path accepts every valid shape.  For tests and
  * measurement.
  */
 int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
@@ -445,6 +448,21 @@ int w4a16_load_quantized(const char *qw_path, const char *sc_path, int64_t N, in
  */
 int w4a16_save_quantized(const char *qw_path, const char *sc_path, int64_t N, int64_t K,
                          int32_t group, const int32_t *qweight, const float *scales);
+
+/*
+ * Measurement helper, not part of the GEMM: one launch that streams n <= 4
+ * DEVICE segments ptrs[i] (16-byte aligned) of bytes[i] bytes (multiples of
+ * 16; host arrays of n entries) with `loads` nontemporal 16-byte loads per
+ * thread (1, 2, 4, 8 or 16, all issued before any is used) and `threads`
+ * threads per block (64..1024, a multiple of 64), and writes at most one
+ * word to `sink` (DEVICE, 4 bytes).  A benchmark times it over the buffers a
+ * GEMM call reads (X, qweight, scales) to measure the streaming-read ceiling
+ * of one launch of that size.  Enqueued on `stream`; W4A16_ERR_ARG for bad
+ * counts, shapes or NULL pointers, W4A16_ERR_ALIGN for misaligned segments or
+ * sizes.
+ */
+int w4a16_read_floor(const void *const *ptrs, const int64_t *bytes, int32_t n, int32_t threads,
+                     int32_t loads, void *sink, void *stream);
 
 #ifdef __cplusplus
 }

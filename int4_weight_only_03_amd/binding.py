@@ -24,6 +24,7 @@ W4A16_PATH_AUTO = 0
 W4A16_PATH_GEMV = 1
 W4A16_PATH_TILE = 2
 W4A16_PATH_SPLIT = 3
+W4A16_PATH_GEMV_FMA = 4
 
 _lib = None
 
@@ -85,6 +86,8 @@ _SIGS = {
                             ctypes.c_void_p], ctypes.c_int),
     "w4a16_gemm_grouped_packed": ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
                                   [ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
+    "w4a16_read_floor": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "w4a16_load_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "w4a16_save_quantized": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
@@ -563,3 +566,18 @@ def w4a16_gemm_split_packed(X, packed, N: int, Y=None, workspace=None, stream=No
 def w4a16_gemm(X, qweight, scales, Y=None, stream=None):
     """Y = X . dequant(qweight, scales)^T on the device (path chosen by the library)."""
     return w4a16_gemm_path(X, qweight, scales, Y, W4A16_PATH_AUTO, stream)
+
+
+def w4a16_read_floor(buffers, sink, threads: int = 256, loads: int = 4, stream=None):
+    """Measurement helper: one launch streaming the device tensors in `buffers`
+    (up to 4, 16-byte aligned, sizes multiples of 16 bytes); `sink` is a device
+    tensor of at least 4 bytes."""
+    import torch
+    if not 1 <= len(buffers) <= 4:
+        raise ValueError("1 to 4 buffers")
+    ptrs = (ctypes.c_void_p * len(buffers))(*[b.data_ptr() for b in buffers])
+    sizes = (ctypes.c_int64 * len(buffers))(*[b.numel() * b.element_size() for b in buffers])
+    st = load().w4a16_read_floor(ptrs, sizes, len(buffers), threads, loads, sink.data_ptr(),
+                                 _stream_ptr(stream, sink.device))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_read_floor")

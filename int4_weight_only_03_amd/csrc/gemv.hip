@@ -429,6 +429,11 @@ hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scal
   return launch<false>(X, qweight, scales, Y, M, N, K, stream);
 }
 
+hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                           int M, int N, int K, hipStream_t stream) {
+  return launch<false>(X, qweight, scales, Y, M, N, K, stream);
+}
+
 hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const float *scales,
                               float *Y, int M, int F, int K, hipStream_t stream) {
   if (gemv_mfma_supported(M, K))  // matrix-core decode GEMV (gemv_mfma.hip)

@@ -79,15 +79,42 @@ int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
 
 int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, void *stream) {
-  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_TILE)
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_TILE &&
+      path != W4A16_PATH_GEMV_FMA)
     return W4A16_ERR_ARG;
   int st = validate_gemm(X, qweight, scales, Y, M, N, K, group);
   if (st != W4A16_OK || M == 0 || N == 0) return st;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (path == W4A16_PATH_GEMV)
-                     ? w4a16::launch_gemv(X, qweight, scales, Y, int(M), int(N), int(K), s)
-                     : w4a16::launch_tile(X, qweight, scales, Y, int(M), int(N), int(K), s);
+  hipError_t e;
+  switch (path) {
+    case W4A16_PATH_GEMV:
+      e = w4a16::launch_gemv(X, qweight, scales, Y, int(M), int(N), int(K), s);
+      break;
+    case W4A16_PATH_GEMV_FMA:
+      e = w4a16::launch_gemv_fma(X, qweight, scales, Y, int(M), int(N), int(K), s);
+      break;
+    default:
+      e = w4a16::launch_tile(X, qweight, scales, Y, int(M), int(N), int(K), s);
+  }
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_read_floor(const void *const *ptrs, const int64_t *bytes, int32_t n, int32_t threads,
+                     int32_t loads, void *sink, void *stream) {
+  if (!ptrs || !bytes || !sink || n < 1 || n > 4) return W4A16_ERR_ARG;
+  if (threads < 64 || threads > 1024 || threads % 64 != 0) return W4A16_ERR_ARG;
+  if (loads != 1 && loads != 2 && loads != 4 && loads != 8 && loads != 16) return W4A16_ERR_ARG;
+  if (!aligned(sink, 4)) return W4A16_ERR_ALIGN;
+  long b[4];
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i] || bytes[i] < 0) return W4A16_ERR_ARG;
+    if (!aligned(ptrs[i], 16) || bytes[i] % 16 != 0) return W4A16_ERR_ALIGN;
+    b[i] = long(bytes[i]);
+  }
+  hipError_t e = w4a16::launch_read_floor(ptrs, b, n, threads, loads,
+                                          static_cast<unsigned *>(sink),
+                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

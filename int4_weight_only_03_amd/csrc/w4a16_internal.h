@@ -92,6 +92,17 @@ hipError_t launch_grouped(const float *X, const int32_t *token_index, const int3
                           const int32_t *qweight, const float *scales, float *Y, int T, int R,
                           int E, int N, int K, hipStream_t stream);
 
+// the fp32 FMA GEMV kernels whatever M and K (the matrix-core GEMV is not
+// considered)
+hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                           int M, int N, int K, hipStream_t stream);
+
+// Measurement helper: one launch streaming n <= 4 device segments (16-byte
+// aligned, byte counts multiples of 16) with `loads` 16-byte loads per thread
+// and `threads` threads per block; sink receives at most one word.
+hipError_t launch_read_floor(const void *const *ptrs, const long *bytes, int n, int threads,
+                             int loads, unsigned *sink, hipStream_t stream);
+
 // Largest M the GEMV path is chosen for by default (the fp32 FMA GEMV); up
 // to kGemvMfmaMaxM when the matrix-core GEMV takes the shape.
 constexpr int kGemvMaxM = 4;

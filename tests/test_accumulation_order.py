@@ -11,10 +11,11 @@ from kernel code), with each product rounded to fp32 before it is added
 (more roundings than the matrix instructions make):
 
 * tiled kernel: per 32-row output tile, each matrix instruction adds two
-  products (k = 32g + i and 32g + 16 + i), 16 instructions per group; the
-  instructions of 8 groups accumulate from zero into a block sum that is then
-  added to the running total; with the K range split over waves, the waves'
-  totals are added in wave order;
+  products (k = 32g + 8v + c and 32g + 8v + 4 + c for instruction 4v + c),
+  16 instructions per group; the instructions of 8 groups accumulate from zero
+  into block sums (one chain, or two chains that take alternate groups, added
+  in chain order) that are then added to the running total; with the K range
+  split over waves, the waves' totals are added in wave order;
 * matrix-core kernels (split path, grouped, small-M, decode GEMV on packed
   weights): each group's 32 products summed from zero, then one fp32 add of
   the group sum per group into the running total;
@@ -57,7 +58,7 @@ def ratio(y, x, w):
     return float(np.max(np.abs(y.astype(np.float64) - exact) / (1e-5 * T + 1e-6)))
 
 
-def tiled_order(x, w, block_groups, waves=1):
+def tiled_order(x, w, block_groups, waves=1, chains=1):
     P = (x * w).astype(f32)
     O, K = P.shape
     G = K // 32
@@ -65,16 +66,19 @@ def tiled_order(x, w, block_groups, waves=1):
     for wv in range(waves):
         g0, g1 = G * wv // waves, G * (wv + 1) // waves
         run = np.zeros(O, f32)
-        blk = np.zeros(O, f32)
+        blk = [np.zeros(O, f32) for _ in range(chains)]
         for g in range(g0, g1):
-            for i in range(16):
-                blk = (blk + P[:, 32 * g + i]).astype(f32)
-                blk = (blk + P[:, 32 * g + 16 + i]).astype(f32)
+            c = (g - g0) % chains
+            for v in range(4):
+                for i in range(4):
+                    blk[c] = (blk[c] + P[:, 32 * g + 8 * v + i]).astype(f32)
+                    blk[c] = (blk[c] + P[:, 32 * g + 8 * v + 4 + i]).astype(f32)
             if block_groups and ((g - g0) % block_groups == block_groups - 1 or g + 1 == g1):
-                run = (run + blk).astype(f32)
-                blk = np.zeros(O, f32)
+                for c in range(chains):
+                    run = (run + blk[c]).astype(f32)
+                    blk[c] = np.zeros(O, f32)
         if not block_groups:
-            run = blk
+            run = blk[0]
         total = (total + run).astype(f32)
     return total
 
@@ -120,7 +124,7 @@ def test_header_limit_is_the_emulated_one(lib):
 def test_tiled_blocks_stay_inside(K):
     x, w = coherent(K)
     assert ratio(tiled_order(x, w, 8), x, w) <= 0.2             # 128 x 128 tiles, one wave
-    assert ratio(tiled_order(x, w, 8, waves=8), x, w) <= 0.2    # skinny tiles, 8 waves
+    assert ratio(tiled_order(x, w, 8, waves=8, chains=2), x, w) <= 0.2  # skinny, 8 waves
 
 
 def test_unblocked_chain_fails_at_the_limit():
