@@ -322,7 +322,8 @@ class Problem:
         wl = self.wl
         return resolved in LIMB_PATHS or (
             resolved in ("gemv", "swiglu")
-            and self.pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) == self.pkg.W4A16_GEMV_MFMA)
+            and self.pkg.w4a16_gemv_kernel(wl.M, wl.N, wl.K) in (self.pkg.W4A16_GEMV_MFMA,
+                                                                 self.pkg.W4A16_GEMV_SKINNY))
 
     def read_floor(self, steps: int, warmup: int) -> dict:
         """Best plain streaming read of the same X, qweight and scales buffers."""

@@ -76,9 +76,8 @@ extern "C" {
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
-#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly GEMV; for M <= 8 and
-                                 K <= 8192 on the 4x4x4 fp16 matrix instructions
-                                 (w4a16_gemv_kernel) */
+#define W4A16_PATH_GEMV 1     /* decode/verify path (M <= 64): dequant-on-the-fly kernels that
+                                 stream the weights once; which one: w4a16_gemv_kernel */
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
 #define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
                                  exact (q - 8) codes and two fp16 limbs of each activation */
@@ -335,7 +334,15 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
                                  into [2^14, 2^15)) before the split, so the limbs hold 22
                                  significant bits; products exact in fp32, fp32 accumulation,
                                  one fp32 multiply per (row, group) applies scale * 2^-e */
-#define W4A16_GEMV_FMA 2      /* otherwise: one fp32 FMA per weight, activations in VGPRs */
+#define W4A16_GEMV_FMA 2      /* M <= 2 with K > 8192, or M > 64 forced onto the GEMV path:
+                                 one fp32 FMA per weight, activations in VGPRs */
+#define W4A16_GEMV_SKINNY 3   /* 3 <= M <= 64 otherwise (the tree-verification batches):
+                                 v_mfma_f32_16x16x32_f16 on exact weight codes and two fp16
+                                 limbs of each activation, prescaled by a power of two per
+                                 row and step of 4 groups (2 with more than 16 rows), the low
+                                 limb x2^11 and met by the codes x2^-11; fp32 accumulation;
+                                 8 waves of a workgroup split K and add their partial tiles
+                                 in order; no workspace */
 
 /* The kernel W4A16_PATH_GEMV runs for an M x N x K shape (one of W4A16_GEMV_*), or 0
  * for a shape w4a16_gemm refuses.  Host only; no GPU use.  (Decode GEMV: the pages'
@@ -345,8 +352,7 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
 
 /* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE): the GEMV
- * path for M <= 4, and for M <= 8 when it runs the matrix-core kernel
- * (K <= 8192); the tiled path otherwise. */
+ * path for M <= 64, the tiled path otherwise. */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 
 /*

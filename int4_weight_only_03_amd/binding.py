@@ -226,6 +226,7 @@ W4A16_GROUPED_GEMV = 3
 
 W4A16_GEMV_MFMA = 1
 W4A16_GEMV_FMA = 2
+W4A16_GEMV_SKINNY = 3
 
 
 def w4a16_gemv_kernel(M: int, N: int, K: int) -> int:

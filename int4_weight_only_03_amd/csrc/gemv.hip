@@ -422,11 +422,19 @@ hipError_t launch(const float *X, const int32_t *qweight, const float *scales, f
 
 }  // namespace
 
+int gemv_kernel(int M, int K) {
+  if (gemv_mfma_supported(M, K)) return W4A16_GEMV_MFMA;  // matrix-core decode GEMV
+  if (M >= 3 && skinny_supported(M)) return W4A16_GEMV_SKINNY;  // skinny.hip
+  return W4A16_GEMV_FMA;
+}
+
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream) {
-  if (gemv_mfma_supported(M, K))  // matrix-core decode GEMV (gemv_mfma.hip)
-    return launch_gemv_mfma(X, qweight, scales, Y, M, N, K, stream);
-  return launch<false>(X, qweight, scales, Y, M, N, K, stream);
+  switch (gemv_kernel(M, K)) {
+    case W4A16_GEMV_MFMA: return launch_gemv_mfma(X, qweight, scales, Y, M, N, K, stream);
+    case W4A16_GEMV_SKINNY: return launch_skinny(X, qweight, scales, Y, M, N, K, stream);
+    default: return launch<false>(X, qweight, scales, Y, M, N, K, stream);
+  }
 }
 
 hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *scales, float *Y,

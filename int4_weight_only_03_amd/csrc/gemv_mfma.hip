@@ -54,21 +54,6 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMxMaxGroups = 256;  // 16 waves of 16 groups: K <= 8192
 
-// Limbs of 8 activations a = x[k..k+3], c = x[k+4..k+7] in the order the
-// nibble conversion produces (x0 x4 x1 x5 x2 x6 x3 x7):
-// hi = f16(x * 2^e), lo = f16(x * 2^(e+11) - 2^11 * hi)  (= f16((x * 2^e - hi) * 2^11);
-// both products by powers of two and the difference are exact in fp32).
-__device__ __forceinline__ void split_block_wide(const float4 a, const float4 c, int e, half8_t &h,
-                                                 half8_t &l) {
-  const float v[8] = {a.x, c.x, a.y, c.y, a.z, c.z, a.w, c.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const _Float16 hv = (_Float16)ldexpf(v[i], e);
-    h[i] = hv;
-    l[i] = (_Float16)__builtin_fmaf((float)hv, -2048.0f, ldexpf(v[i], e + 11));
-  }
-}
-
 // LDS: per wave [16 groups][limb rows of one A operand][4 quarters] of 8 fp16:
 // 2 limb rows for MT = 1 (2 KB), 4 otherwise (4 KB); with MT > 2 the A
 // operands pass through it one after the other.  Once a wave has read its

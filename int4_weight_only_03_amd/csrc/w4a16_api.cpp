@@ -46,10 +46,8 @@ int validate_gemm(const float *X, const int32_t *qweight, const float *scales, f
 }
 
 int select_path(int64_t M, int64_t K) {
-  if (M <= w4a16::kGemvMaxM) return W4A16_PATH_GEMV;
-  if (M <= w4a16::kGemvMfmaMaxM && K <= W4A16_MAX_K && w4a16::gemv_mfma_supported(int(M), int(K)))
-    return W4A16_PATH_GEMV;
-  return W4A16_PATH_TILE;
+  (void)K;
+  return M <= w4a16::kGemvMaxM ? W4A16_PATH_GEMV : W4A16_PATH_TILE;
 }
 
 }  // namespace
@@ -316,7 +314,7 @@ int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
-  return w4a16::gemv_mfma_supported(int(M), int(K)) ? W4A16_GEMV_MFMA : W4A16_GEMV_FMA;
+  return w4a16::gemv_kernel(int(M), int(K));
 }
 
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/w4a16.h"
+
 namespace w4a16 {
 
 constexpr int kGroup = 32;
@@ -14,6 +16,9 @@ constexpr int kGroup = 32;
 // Decode/verify path: dequant-on-the-fly GEMV with activations held in VGPRs.
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream);
+
+// The kernel launch_gemv runs for M rows and K (one of W4A16_GEMV_*).
+int gemv_kernel(int M, int K);
 
 // Decode GEMV (M <= 8, K <= 8192) on the 4x4x4 fp16 matrix instructions:
 // exact weight codes, two fp16 limbs of each group-prescaled activation.
@@ -25,6 +30,14 @@ hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float 
 // the same with the fused gate/up SwiGLU epilogue (W: 2F rows, gate then up; Y[M][F])
 hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const float *scales,
                                    float *Y, int M, int F, int K, hipStream_t stream);
+
+// Skinny GEMM (1 <= M <= kSkinnyMaxM) on the fp16 matrix instructions: exact
+// weight codes, two fp16 limbs of each activation prescaled per row and step
+// of 4 groups, fp32 accumulation; no workspace.
+constexpr int kSkinnyMaxM = 64;
+bool skinny_supported(int M);
+hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                         int M, int N, int K, hipStream_t stream);
 
 // Tiled path: fp32 MFMA (32x32x2) on weight tiles dequantized into registers.
 hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
@@ -103,9 +116,7 @@ hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *
 hipError_t launch_read_floor(const void *const *ptrs, const long *bytes, int n, int threads,
                              int loads, unsigned *sink, hipStream_t stream);
 
-// Largest M the GEMV path is chosen for by default (the fp32 FMA GEMV); up
-// to kGemvMfmaMaxM when the matrix-core GEMV takes the shape.
-constexpr int kGemvMaxM = 4;
-constexpr int kGemvMfmaMaxM = 8;
+// Largest M the GEMV path (decode GEMVs and the skinny kernel) is chosen for.
+constexpr int kGemvMaxM = kSkinnyMaxM;
 
 }  // namespace w4a16

@@ -1,0 +1,134 @@
+"""GPU parity of the skinny matrix-core kernel (W4A16_GEMV_SKINNY: 3 <= M <= 64
+outside the decode GEMV's range), the kernel w4a16_gemm runs for the
+tree-verification batches, against the CPU oracle through the C ABI."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_only_03_amd import binding  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run(X, qw, sc, dev, Y=None):
+    out = binding.w4a16_gemm(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(Y, X, qw, sc, what):
+    v = oracle.compare(Y, X, qw, sc)
+    say(f"{what}: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], (what, v)
+
+
+# rows: one or two 16-row subtiles, one or several row blocks; N: ragged, one
+# or two 16-column subtiles per wave; K: fewer groups than waves, steps past G,
+# group counts not a multiple of the step
+MS = [9, 16, 17, 31, 32, 33, 48, 63, 64]
+NK = [(1, 32), (17, 96), (33, 224), (257, 2080), (300, 7168), (4096, 1056)]
+
+
+@pytest.mark.parametrize("M", MS)
+@pytest.mark.parametrize("N,K", NK)
+def test_shapes_against_oracle(dev, M, N, K):
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_GEMV
+    say(f"skinny M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M * 131 + N * 7 + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [3, 5, 8])
+def test_small_m_past_the_decode_gemv(dev, M):
+    N, K = 100, 8192 + 96
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_SKINNY
+    X, W = workloads.random_case(M, N, K, seed=M + 3)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 96, 7168), (20, 50, 224), (40, 33, 2048)])
+def test_integer_inputs_exact(dev, M, N, K):
+    X, nib = workloads.integer_case(M, N, K, seed=K + N + M)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), dtype=np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+def test_deterministic_guard_band_and_scaling(dev):
+    M, N, K = 37, 45, 1024
+    X, W = workloads.random_case(M, N, K, seed=21)
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    a = run(X, qw, sc, dev, Y)
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    b = run(X, qw, sc, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = run((X * np.float32(8.0)).astype(np.float32), qw, sc, dev)
+    assert np.array_equal(c, a * np.float32(8.0))
+    check(a, X, qw, sc, "skinny guarded")
+
+
+def test_step_magnitudes_far_apart(dev):
+    # each step of 4 groups (2 with more than 16 rows) at its own power of two,
+    # zero steps, subnormal entries, and a step spanning 2^26 inside
+    rng = np.random.default_rng(12)
+    M, N, K = 24, 130, 4096
+    G = K // 32
+    X = rng.standard_normal((M, K))
+    exps = rng.integers(-100, 101, (M, G // 4))
+    X = X * np.repeat(np.exp2(exps.astype(np.float64)), 128, axis=1)
+    X[:, 128 * 3:128 * 4] = 0.0
+    X[0, 128 * 5:128 * 6] = rng.standard_normal(128) * 1e-42  # fp32 subnormals
+    X[1, 128 * 7:128 * 8] *= np.exp2(-rng.integers(0, 27, 128).astype(np.float64))
+    X = X.astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, "skinny magnitudes")
+
+
+def test_nonfinite_rows(dev):
+    M, N, K = 20, 40, 512
+    X, W = workloads.random_case(M, N, K, seed=13)
+    X[2, 7] = np.inf
+    X[11, 300] = np.nan
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, dev)
+    assert np.all(np.isnan(Y[2])) and np.all(np.isnan(Y[11]))
+    keep = [i for i in range(M) if i not in (2, 11)]
+    check(Y[keep], X[keep], qw, sc, "skinny finite rows")
+
+
+def test_verify_tree_every_output(dev):
+    X, W = workloads.make("verify_tree")
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, "verify_tree skinny")

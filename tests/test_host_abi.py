@@ -40,25 +40,30 @@ def test_status_strings(lib):
 
 
 def test_gemv_kernel(lib):
-    # matrix-core decode GEMV for M <= 8 and K <= 8192, the fp32 FMA kernels otherwise
+    # matrix-core decode GEMV for M <= 8 and K <= 8192; the skinny matrix-core
+    # kernel for 3 <= M <= 64 otherwise; the fp32 FMA GEMV for M <= 2 with long K
+    # (and for M > 64 forced onto the GEMV path)
     assert binding.w4a16_gemv_kernel(1, 4096, 7168) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(2, 7, 8192) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(2, 64, 1 << 17) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(3, 64, 8192 + 32) == binding.W4A16_GEMV_SKINNY
     assert binding.w4a16_gemv_kernel(4, 64, 256) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(8, 64, 256) == binding.W4A16_GEMV_MFMA
-    assert binding.w4a16_gemv_kernel(9, 64, 256) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(9, 64, 256) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(64, 4096, 7168) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(65, 64, 256) == binding.W4A16_GEMV_FMA
     assert binding.w4a16_gemv_kernel(0, 64, 256) == 0
     assert binding.w4a16_gemv_kernel(1, 64, 250) == 0
     assert binding.w4a16_gemv_kernel(1, 0, 256) == 0
 
 
 def test_select_path(lib):
-    assert binding.w4a16_select_path(1, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(4, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(5, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(8, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(5, 4096, 8192 + 32) == binding.W4A16_PATH_TILE
-    assert binding.w4a16_select_path(9, 4096, 7168) == binding.W4A16_PATH_TILE
+    # the decode/verify path for M <= 64, the tiled path above
+    for M in (1, 4, 5, 8, 9, 17, 64):
+        assert binding.w4a16_select_path(M, 4096, 7168) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(5, 4096, 8192 + 32) == binding.W4A16_PATH_GEMV
+    assert binding.w4a16_select_path(65, 4096, 7168) == binding.W4A16_PATH_TILE
     assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE
 
 
