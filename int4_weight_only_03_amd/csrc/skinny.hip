@@ -47,32 +47,22 @@ namespace w4a16 {
 namespace {
 
 #ifndef W4A16_SK_WAVES
-#define W4A16_SK_WAVES 16
+#define W4A16_SK_WAVES 8
 #endif
 #ifndef W4A16_SK_P
 #define W4A16_SK_P 1
 #endif
 constexpr int kSkWaves = W4A16_SK_WAVES;  // waves per workgroup, splitting the K range
-constexpr int kSkSG = 2;         // groups per step (one power of two per row and step)
-constexpr int kSkP = W4A16_SK_P;  // steps in flight per wave (LDS slots)
-// one slot: the step's activations (16*MT rows x 256 B), weight words (32 W
-// rows x 32 B) and scales (32 W rows x 8 B)
+constexpr int kSkP = W4A16_SK_P;          // steps in flight per wave (LDS slots)
+constexpr int kSkSG = 4;                  // groups per step
+// one slot: the step's activations (16*MT rows x 512 B), weight words (16*NT
+// W rows x 64 B) and scales (16*NT W rows x 16 B)
 __host__ __device__ constexpr int sk_xbytes(int MT) { return 16 * MT * kSkSG * 128; }
-// weight and scale copies per step: one per 32 rows of W (at least one)
-__host__ __device__ constexpr int sk_wcopies(int NT) { return NT < 2 ? 1 : NT / 2; }
-__host__ __device__ constexpr int sk_wbytes(int NT) { return sk_wcopies(NT) * 32 * kSkSG * 16; }
-__host__ __device__ constexpr int sk_sbytes(int NT) { return sk_wcopies(NT) * 32 * kSkSG * 4; }
 __host__ __device__ constexpr int sk_slot(int MT, int NT) {
-  return sk_xbytes(MT) + sk_wbytes(NT) + sk_sbytes(NT);
+  return sk_xbytes(MT) + NT * 16 * kSkSG * 16 + NT * 16 * kSkSG * 4;
 }
 
 typedef __attribute__((address_space(3))) void sk_lds_void;
-
-// LDS: per wave kSkP slots and 16*MT row factors; the partial tiles of the
-// final reduction reuse the slots
-__host__ __device__ constexpr int sk_lds_bytes(int MT, int NT) {
-  return kSkWaves * (kSkP * sk_slot(MT, NT) + 16 * MT * 4);
-}
 
 // s_waitcnt with vmcnt = VM (lgkmcnt, expcnt not waited for)
 template <int VM>
@@ -111,111 +101,153 @@ __device__ __forceinline__ void sk_split2(float t0, float t1, float k, float m, 
       : "v"(t0), "v"(t1), "v"(k), "v"(m));
 }
 
-template <int MT, int NT, int SG, int P>
+template <int MT, int NT, int P>
 __global__ void __launch_bounds__(64 * kSkWaves)
 skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
           const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G,
           int tiles_n) {
-  extern __shared__ __align__(16) unsigned char sk_lds[];
-  constexpr int kRows = 16 * MT;                 // rows of X staged per wave
-  constexpr int kRowBytes = SG * 128;            // one row of one step
-  constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per staged row
-  constexpr int kCopies = kRows * kRowBytes / 1024;  // 1 KB activation copies per step
+  constexpr int SG = kSkSG;
   constexpr int kSlot = sk_slot(MT, NT);
-  constexpr int kWC = sk_wcopies(NT);
-  static_assert(SG == kSkSG && kChunks == 16, "a staged row is 16 chunks");
-  // VMEM operations per step: the activation copies, one weight copy, one
-  // scale copy
-  constexpr int kStepOps = kCopies + 2 * kWC;
+  static_assert(P >= 1 && P <= 2, "ring depth");
+  // Each ring entry's slots and the row factors are LDS objects of their
+  // own, so that the compiler can tell a read of one from the direct copies
+  // into another (else it waits for every copy in flight before any LDS
+  // read, the row factors' included).
+  __shared__ __align__(16) unsigned char sk_ring0[kSkWaves * kSlot];
+  __shared__ __align__(16) unsigned char sk_ring1[P > 1 ? kSkWaves * kSlot : 16];
+  __shared__ __align__(16) float sk_finv[kSkWaves * 16 * MT];
+  constexpr int kRows = 16 * MT;         // rows of X staged per wave
+  constexpr int kRowBytes = SG * 128;    // one row of one step: 32 chunks of 16 bytes
+  constexpr int kCopies = kRows * kRowBytes / 1024;  // 1 KB activation copies per step
+  constexpr int kWOff = sk_xbytes(MT);               // weight words in the slot
+  constexpr int kSOff = kWOff + NT * 1024;           // scales in the slot
+  // VMEM operations per step: the activation copies, NT weight copies, NT
+  // scale copies
+  constexpr int kStepOps = kCopies + 2 * NT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int c = lane & 15, R = lane >> 4;
   const int nb = blockIdx.x % tiles_n, mb = blockIdx.x / tiles_n;
   const int m0 = mb * 16 * MT, n0 = nb * 16 * NT;
-  const long K = long(G) * kGroup;
-  const int S = (G + SG - 1) / SG;  // steps
+  const int S = G / SG;  // whole steps
   const int s0 = int(long(S) * wave / kSkWaves), s1 = int(long(S) * (wave + 1) / kSkWaves);
-  unsigned char *slots = sk_lds + wave * (P * kSlot);             // this wave's staging slots
-  float *finv = reinterpret_cast<float *>(sk_lds + kSkWaves * P * kSlot) + wave * kRows;
+  // this wave's staging slot of ring entry v
+  auto slot_of = [&](int v) -> unsigned char * {
+    return (v == 0 ? sk_ring0 : sk_ring1) + wave * kSlot;
+  };
+  float *finv = sk_finv + wave * kRows;
 
   // Activation copies: copy j, lane i writes LDS bytes 16 i .. 16 i + 15 of
-  // the slot's kilobyte j: staged row rho = 4 j + i / 16, physical chunk
-  // p = i % 16, which holds the row's logical chunk p ^ (rho & 15) (an XOR
+  // the slot's kilobyte j: staged row rho = 2 j + i / 32, physical chunk
+  // p = i % 32, which holds the row's logical chunk p ^ (rho & 15) (an XOR
   // swizzle: the 16 rows an operand read touches at one logical chunk fall in
-  // 16 distinct chunks, hence distinct LDS banks; each lane quad still reads
-  // 64 contiguous bytes).  Rows past M read row M-1.  Every copy's address is
-  // a wave-uniform base (the step's first group) plus a fixed per-lane byte
-  // offset below 2^32 (X holds at most 64 rows of 2^17 floats).
+  // 16 distinct chunks of one 256-byte window, hence distinct LDS banks).
+  // Rows past M read row M-1.  Every copy's address is a wave-uniform base
+  // (the step's first group) plus a fixed per-lane byte offset below 2^32 (X
+  // holds at most 64 rows of 2^17 floats).
   uint32_t xoff[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
-    const int rho = 4 * j + lane / 16;
-    const int xchunk = (lane & 15) ^ (rho & 15);
-    xoff[j] = uint32_t(std::min(m0 + rho, M - 1)) * uint32_t(K * 4) +
-              uint32_t(128 * (xchunk >> 3) + 16 * (xchunk & 7));
+    const int rho = 2 * j + lane / 32;
+    const int L = (lane & 31) ^ (rho & 15);
+    xoff[j] = uint32_t(std::min(m0 + rho, M - 1)) * uint32_t(G) * 128u + 16u * uint32_t(L);
   }
-  // Weight copy jw: lane i writes the 16 bytes of group (i & 1) of the step
-  // of W row n0 + 32 jw + i / 2 (rows past N read row N-1).  Scale copy jw:
-  // lane i writes the scale of group (i & 1) of the same row.  Offsets
-  // relative to the tile's first row (below 2^23 bytes).
-  uint32_t woff[kWC], soff[kWC];
+  // Weight copy t: lane i writes 16 bytes at slot offset 1024 t + 16 i: W row
+  // n0 + 16 t + i / 4, position i % 4 of that row's 64 bytes, which holds
+  // group (i % 4 - i / 16) % 4 of the step (each row's groups rotated by
+  // row / 4, so that the 16 rows a read touches at one group fall in distinct
+  // banks).  Scale copy t: lane i writes 4 bytes at offset 256 t + 4 i of the
+  // scales: the scale of group i % 4 of the same row.  Rows past N read row
+  // N-1.  Offsets relative to the tile's first row (below 2^23 bytes).
+  const int wg = ((lane & 3) - (lane >> 4)) & 3;  // group of this lane's weight copy
+  uint32_t woff[NT], soff[NT];
 #pragma unroll
-  for (int jw = 0; jw < kWC; ++jw) {
-    const uint32_t wrow = uint32_t(std::min(n0 + 32 * jw + lane / 2, N - 1) - n0);
-    woff[jw] = (wrow * uint32_t(G) + uint32_t(lane & 1)) * 16u;
-    soff[jw] = (wrow * uint32_t(G) + uint32_t(lane & 1)) * 4u;
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t wrow = uint32_t(std::min(n0 + 16 * t + lane / 4, N - 1) - n0);
+    woff[t] = (wrow * uint32_t(G) + uint32_t(wg)) * 16u;
+    soff[t] = (wrow * uint32_t(G) + uint32_t(lane & 3)) * 4u;
   }
   const char *wtile = reinterpret_cast<const char *>(qw) + long(n0) * G * 16;
   const char *stile = reinterpret_cast<const char *>(sc) + long(n0) * G * 4;
 
-  // Step s's copies.  Only the last step of an odd G reaches past the end of
-  // a row: there the second group's chunks re-read group G-1 (masked).
-  auto load = [&](int v, int s) {
-    unsigned char *slot = slots + v * kSlot;
+  // Step s's copies into slot v (kTail: the step past the whole steps, whose
+  // groups past G re-read group G-1, masked later).  The offsets pass
+  // through an empty asm so that their zero extension stays beside the
+  // copies, which then take the scalar-base form.
+  auto load = [&](int v, int s, auto kTail) {
+    constexpr bool tail = decltype(kTail)::value;
+    unsigned char *slot = slot_of(v);
     const long gs = long(s) * SG;
-    // (the offsets pass through an empty asm so that their zero extension
-    // stays beside the loads, which then take the scalar-base form)
 #pragma unroll
     for (int j = 0; j < kCopies; ++j) sk_opaque(xoff[j]);
 #pragma unroll
-    for (int jw = 0; jw < kWC; ++jw) {
-      sk_opaque(woff[jw]);
-      sk_opaque(soff[jw]);
+    for (int t = 0; t < NT; ++t) {
+      sk_opaque(woff[t]);
+      sk_opaque(soff[t]);
     }
-    if (SG * (s + 1) <= G) {
+    if (!tail) {
       const char *xb = reinterpret_cast<const char *>(X) + gs * 128;
 #pragma unroll
       for (int j = 0; j < kCopies; ++j) {
         const char *src = xb + xoff[j];
-        __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + 1024 * j), 16, 0, 0);
       }
 #pragma unroll
-      for (int jw = 0; jw < kWC; ++jw) {
-        const char *wsrc = wtile + gs * 16 + woff[jw];
-        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + sk_xbytes(MT) + 1024 * jw),
-                                         16, 0, 0);
-        const char *ssrc = stile + gs * 4 + soff[jw];
-        __builtin_amdgcn_global_load_lds(
-            ssrc, (sk_lds_void *)(slot + sk_xbytes(MT) + sk_wbytes(NT) + 256 * jw), 4, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        const char *wsrc = wtile + gs * 16 + woff[t];
+        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0, 0);
+        const char *ssrc = stile + gs * 4 + soff[t];
+        __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
       }
     } else {
-      const char *xb = reinterpret_cast<const char *>(X) + (G - 1) * 128L;
+      const char *xb = reinterpret_cast<const char *>(X);
 #pragma unroll
       for (int j = 0; j < kCopies; ++j) {
-        const uint32_t q = uint32_t(((lane & 15) ^ ((4 * j + lane / 16) & 15)) >> 3);
-        const char *src = xb + (xoff[j] - 128u * q);
-        __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + j * 1024), 16, 0, 0);
+        const int rho = 2 * j + lane / 32;
+        const uint32_t q = uint32_t(((lane & 31) ^ (rho & 15)) >> 3);  // the chunk's group
+        const char *src =
+            xb + std::min(gs + q, long(G) - 1) * 128 + (xoff[j] - 128u * q);
+        __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + 1024 * j), 16, 0, 0);
       }
-      const uint32_t odd = uint32_t(lane & 1);
+      const long gw = std::min(gs + wg, long(G) - 1), gsc = std::min(gs + (lane & 3), long(G) - 1);
 #pragma unroll
-      for (int jw = 0; jw < kWC; ++jw) {
-        const char *wsrc = wtile + (G - 1) * 16L + (woff[jw] - 16u * odd);
-        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + sk_xbytes(MT) + 1024 * jw),
-                                         16, 0, 0);
-        const char *ssrc = stile + (G - 1) * 4L + (soff[jw] - 4u * odd);
-        __builtin_amdgcn_global_load_lds(
-            ssrc, (sk_lds_void *)(slot + sk_xbytes(MT) + sk_wbytes(NT) + 256 * jw), 4, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        const char *wsrc = wtile + gw * 16 + (woff[t] - 16u * uint32_t(wg));
+        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0, 0);
+        const char *ssrc = stile + gsc * 4 + (soff[t] - 4u * uint32_t(lane & 3));
+        __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
       }
+    }
+  };
+
+  // A step's operands, copied from its slot into registers (after which the
+  // slot can take the next copies): this lane's activations of row 16u + c,
+  // group g, k = 8R .. 8R+7 (logical chunks 8g + 2R and 8g + 2R + 1), word R
+  // of group g of W row 16t + c, and that row's scales of the step's groups.
+  struct Ops {
+    float4 x[MT][SG][2];
+    uint32_t w[NT][SG];
+    float4 sc[NT];
+  };
+  auto fetch = [&](int v, Ops &o) {
+    const unsigned char *slot = slot_of(v);
+#pragma unroll
+    for (int u = 0; u < MT; ++u)
+#pragma unroll
+      for (int g = 0; g < SG; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pch = (8 * g + 2 * R + h) ^ c;  // (16u + c) & 15 == c
+          o.x[u][g][h] =
+              *reinterpret_cast<const float4 *>(slot + (16 * u + c) * kRowBytes + 16 * pch);
+        }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int g = 0; g < SG; ++g)
+        o.w[t][g] = *reinterpret_cast<const uint32_t *>(slot + kWOff + 1024 * t + 64 * c +
+                                                        16 * ((g + (c >> 2)) & 3) + 4 * R);
+      o.sc[t] = *reinterpret_cast<const float4 *>(slot + kSOff + 256 * t + 16 * c);
     }
   };
 
@@ -227,162 +259,121 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[u][t][r] = 0.0f;
 
-  // A step's operands, copied from its slot into registers (after which the
-  // slot can take the next copies): this lane's activations of row 16u + c,
-  // group q, k = 8R .. 8R+7 (logical chunks 8q + 2R and 8q + 2R + 1), word R
-  // of group q of W row 16t + c and that row's scale of group q.
-  struct Ops {
-    float4 x[MT][SG][2];
-    uint32_t w[NT][SG];
-    float sc[NT][SG];
-  };
-  auto fetch = [&](int v, Ops &o) {
-    const unsigned char *slot = slots + v * kSlot;
-    const uint32_t *wst = reinterpret_cast<const uint32_t *>(slot + sk_xbytes(MT));
-    const float *sst = reinterpret_cast<const float *>(slot + sk_xbytes(MT) + sk_wbytes(NT));
-#pragma unroll
-    for (int u = 0; u < MT; ++u)
-#pragma unroll
-      for (int q = 0; q < SG; ++q)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int rho = 16 * u + c;
-          const int pch = (8 * q + 2 * R + h) ^ c;  // rho & 15 == c
-          o.x[u][q][h] = *reinterpret_cast<const float4 *>(slot + rho * kRowBytes + 16 * pch);
-        }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int q = 0; q < SG; ++q) {
-        o.w[t][q] = wst[((16 * t + c) * SG + q) * 4 + R];
-        o.sc[t][q] = sst[(16 * t + c) * SG + q];
-      }
-  };
-
-  // one step: kMask when some of its groups may lie past G (the last step
-  // only), whose activations and scales then count as zero
+  // one step, in two pairs of groups (one power of two per row and pair);
+  // kMask for the step past the whole steps, whose groups past G count as
+  // zero
   auto process = [&](int s, const Ops &o, auto kMask) {
     constexpr bool mask = decltype(kMask)::value;
     const int gb = s * SG;
-    float4 xv[MT][SG][2];
 #pragma unroll
-    for (int u = 0; u < MT; ++u)
+    for (int pr = 0; pr < SG / 2; ++pr) {
+      float4 xv[MT][2][2];
 #pragma unroll
-      for (int q = 0; q < SG; ++q)
+      for (int u = 0; u < MT; ++u)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          xv[u][q][h] = (!mask || gb + q < G) ? o.x[u][q][h] : make_float4(0.f, 0.f, 0.f, 0.f);
-    // the step's largest magnitude per row (fmaxf of magnitudes: a NaN is
-    // passed over here and still turns the row's products to NaN), over this
-    // lane's values, then over the row's 4 lanes
-    int e[MT];
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      // a tree of three-operand maxima over the 4 SG values
-      static_assert(SG == 2, "the maximum tree takes 16 values");
-      float v16[16];
-#pragma unroll
-      for (int q = 0; q < SG; ++q)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float4 x4 = xv[u][q][h];
-          v16[8 * q + 4 * h + 0] = x4.x;
-          v16[8 * q + 4 * h + 1] = x4.y;
-          v16[8 * q + 4 * h + 2] = x4.z;
-          v16[8 * q + 4 * h + 3] = x4.w;
-        }
-      const float m0 = sk_absmax3(v16[0], v16[1], v16[2]);
-      const float m1 = sk_absmax3(v16[3], v16[4], v16[5]);
-      const float m2 = sk_absmax3(v16[6], v16[7], v16[8]);
-      const float m3 = sk_absmax3(v16[9], v16[10], v16[11]);
-      const float m4 = sk_absmax3(v16[12], v16[13], v16[14]);
-      const float m5 = sk_absmax3(m0, m1, v16[15]);
-      float mx = sk_absmax3(m2, m3, m4);
-      mx = sk_absmax3(mx, m5, 0.0f);
-      const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-      mx = sk_absmax3(__uint_as_float(h32[0]), __uint_as_float(h32[1]), 0.0f);
-      const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-      mx = sk_absmax3(__uint_as_float(h16[0]), __uint_as_float(h16[1]), 0.0f);
-      // e in [-113, 116]: 2^-e and 2^(e+11) are normal fp32 numbers.  A row
-      // whose step maximum lies below 2^-102 keeps fewer limb bits; its
-      // absolute error stays below 2^-120 of the weights' magnitude.
-      e[u] = std::min(row_exponent(mx), 116);
-      if (R == 0) finv[16 * u + c] = __int_as_float((127 - e[u]) << 23);
-    }
-    // 2^(e+11) per row: x * 2^(e+11) is exact and finite (|x| 2^e < 2^15)
-    float up[MT];
-#pragma unroll
-    for (int u = 0; u < MT; ++u) up[u] = ldexpf(1.0f, e[u] + 11);
-    // the factors of this lane's result rows 4R .. 4R+3 (this wave's own LDS
-    // words: its LDS operations complete in order)
-    float4 fac[MT];
-#pragma unroll
-    for (int u = 0; u < MT; ++u) fac[u] = *reinterpret_cast<const float4 *>(finv + 16 * u + 4 * R);
-
-    float ss[MT][NT][4];  // the step's sum, group scales applied, 2^-e not yet
-#pragma unroll
-    for (int u = 0; u < MT; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ss[u][t][r] = 0.0f;
-    const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int q = 0; q < SG; ++q) {
-      half8_t hi[MT], lo[MT];
+          for (int h = 0; h < 2; ++h)
+            xv[u][q][h] = (!mask || gb + 2 * pr + q < G) ? o.x[u][2 * pr + q][h]
+                                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      // the pair's largest magnitude per row: a tree of three-operand
+      // maxima over this lane's 16 values, then over the row's 4 lanes
+      // (a NaN is passed over here and still turns the row's products to NaN)
+      int e[MT];
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
-        // t = x 2^(e+11) (exact); hi = f16(t 2^-11); lo = f16(t - 2^11 hi), the
-        // difference exact in fp32; order x0 x4 x1 x5 x2 x6 x3 x7
-        const float4 a = xv[u][q][0], b4 = xv[u][q][1];
-        const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b4.x, b4.y, b4.z, b4.w};
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sk_split2(va[i] * up[u], vb[i] * up[u], 0x1p-11f, -2048.0f, hw[i], lw[i]);
-        hi[u] = __builtin_bit_cast(half8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        lo[u] = __builtin_bit_cast(half8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        const float4 a0 = xv[u][0][0], a1 = xv[u][0][1], a2 = xv[u][1][0], a3 = xv[u][1][1];
+        const float t0 = sk_absmax3(a0.x, a0.y, a0.z);
+        const float t1 = sk_absmax3(a0.w, a1.x, a1.y);
+        const float t2 = sk_absmax3(a1.z, a1.w, a2.x);
+        const float t3 = sk_absmax3(a2.y, a2.z, a2.w);
+        const float t4 = sk_absmax3(a3.x, a3.y, a3.z);
+        const float t5 = sk_absmax3(t0, t1, a3.w);
+        float mx = sk_absmax3(t2, t3, t4);
+        mx = sk_absmax3(mx, t5, 0.0f);
+        const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = sk_absmax3(__uint_as_float(h32[0]), __uint_as_float(h32[1]), 0.0f);
+        const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = sk_absmax3(__uint_as_float(h16[0]), __uint_as_float(h16[1]), 0.0f);
+        // e in [-113, 116]: 2^-e and 2^(e+11) are normal fp32 numbers.  A
+        // row whose pair maximum lies below 2^-102 keeps fewer limb bits; its
+        // absolute error stays below 2^-120 of the weights' magnitude.
+        e[u] = std::min(row_exponent(mx), 116);
+        if (R == 0) finv[16 * u + c] = __int_as_float((127 - e[u]) << 23);
       }
+      // 2^(e+11) per row: x * 2^(e+11) is exact and finite (|x| 2^e < 2^15)
+      float up[MT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const half8_t b = nibbles_to_f16(o.w[t][q]);
-        const _Float16 k2 = (_Float16)0x1p-11f;
-        const half8_t b2 = b * half8_t{k2, k2, k2, k2, k2, k2, k2, k2};  // exact in fp16
-        const float sq = (!mask || gb + q < G) ? o.sc[t][q] : 0.0f;
+      for (int u = 0; u < MT; ++u) up[u] = ldexpf(1.0f, e[u] + 11);
+      // the factors of this lane's result rows 4R .. 4R+3 (this wave's own
+      // LDS words: its LDS operations complete in order)
+      float4 fac[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u)
+        fac[u] = *reinterpret_cast<const float4 *>(finv + 16 * u + 4 * R);
+
+      float ss[MT][NT][4];  // the pair's sum, group scales applied, 2^-e not yet
+      const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int g = 2 * pr + q;
+        half8_t hi[MT], lo[MT];
 #pragma unroll
         for (int u = 0; u < MT; ++u) {
-          floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[u], b, zero, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[u], b2, d, 0, 0, 0);
+          // t = x 2^(e+11) (exact); hi = f16(t 2^-11); lo = f16(t - 2^11 hi),
+          // the difference exact in fp32; order x0 x4 x1 x5 x2 x6 x3 x7
+          const float4 a = xv[u][q][0], b4 = xv[u][q][1];
+          const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b4.x, b4.y, b4.z, b4.w};
+          uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ss[u][t][r] = fmaf(sq, d[r], ss[u][t][r]);
+          for (int i = 0; i < 4; ++i)
+            sk_split2(va[i] * up[u], vb[i] * up[u], 0x1p-11f, -2048.0f, hw[i], lw[i]);
+          hi[u] = __builtin_bit_cast(half8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          lo[u] = __builtin_bit_cast(half8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const half8_t b = nibbles_to_f16(o.w[t][g]);
+          const _Float16 k2 = (_Float16)0x1p-11f;
+          const half8_t b2 = b * half8_t{k2, k2, k2, k2, k2, k2, k2, k2};  // exact in fp16
+          const float s4[4] = {o.sc[t].x, o.sc[t].y, o.sc[t].z, o.sc[t].w};
+          const float sq = (!mask || gb + g < G) ? s4[g] : 0.0f;
+#pragma unroll
+          for (int u = 0; u < MT; ++u) {
+            floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[u], b, zero, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[u], b2, d, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              ss[u][t][r] = q == 0 ? sq * d[r] : fmaf(sq, d[r], ss[u][t][r]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      const float f[4] = {fac[u].x, fac[u].y, fac[u].z, fac[u].w};
+      for (int u = 0; u < MT; ++u) {
+        const float f[4] = {fac[u].x, fac[u].y, fac[u].z, fac[u].w};
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[u][t][r] = fmaf(ss[u][t][r], f[r], acc[u][t][r]);
+          for (int r = 0; r < 4; ++r) acc[u][t][r] = fmaf(ss[u][t][r], f[r], acc[u][t][r]);
+      }
     }
   };
 
-  // The ring: slot v holds the steps s with (s - s0) % P == v.  Before a
-  // slot's reads, wait until only the later slots' operations are in flight;
-  // once its reads are done (its operands are in registers), reload it and
-  // only then work on the operands, so that the copies overlap that work.
+  // The ring: slot v holds the steps s with (s - s0) % P == v.  Per step:
+  // wait until only the later slots' operations are in flight; move the
+  // slot's operands into registers; once those reads are done, start the
+  // slot's copies of step s + P; then do the arithmetic, under the copies.
+  // (A wave's last reloads repeat its last step: never used, they keep the
+  // number of operations in flight the same for every step.)
+  const std::false_type whole;
   if (s0 < s1) {
 #pragma unroll
-    for (int v = 0; v < P; ++v) load(v, std::min(s0 + v, s1 - 1));
+    for (int v = 0; v < P; ++v) load(v, std::min(s0 + v, s1 - 1), whole);
   }
-  // whole rings: none of their steps reaches past G (the last step of the K
-  // range is always in the partial ring below, or the wave's last step)
-  const int s_full = std::min(s1, S - 1);
   int s = s0;
-  for (; s + P <= s_full; s += P) {
+  for (; s + P <= s1; s += P) {
 #pragma unroll
     for (int v = 0; v < P; ++v) {
       Ops o;
@@ -393,28 +384,43 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
       asm volatile("" ::: "memory");
       sk_wait_lgkm0();
       asm volatile("" ::: "memory");
-      load(v, std::min(s + v + P, s1 - 1));
+      load(v, std::min(s + v + P, s1 - 1), whole);
       // the reload stays ahead of the step's arithmetic
       __builtin_amdgcn_sched_barrier(0);
-      process(s + v, o, std::false_type{});
+      process(s + v, o, whole);
     }
   }
   asm volatile("" ::: "memory");
   sk_wait_vm<0>();
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int v = 0; v < P; ++v)
+  for (int v = 0; v < P - 1; ++v)
     if (s + v < s1) {
       Ops o;
       fetch(v, o);
-      process(s + v, o, std::true_type{});
+      process(s + v, o, whole);
     }
+  // the groups past the whole steps (G % 4 of them), on the last wave, from
+  // slot 0 (free: every copy of this wave is done and read)
+  if (G % SG != 0 && wave == kSkWaves - 1) {
+    const std::true_type tail;
+    asm volatile("" ::: "memory");
+    sk_wait_lgkm0();
+    asm volatile("" ::: "memory");
+    load(0, S, tail);
+    asm volatile("" ::: "memory");
+    sk_wait_vm<0>();
+    asm volatile("" ::: "memory");
+    Ops o;
+    fetch(0, o);
+    process(S, o, tail);
+  }
 
-  // the waves' partial tiles, added in wave order (the staging slots are free
-  // once every wave is past its loop)
+  // the waves' partial tiles, added in wave order (the slots are free once
+  // every wave is past its loop)
   constexpr int kTile = MT * NT * 4 * 64;
-  static_assert(kTile * kSkWaves * 4 <= kSkWaves * kSkP * kSlot, "partials fit the slots");
-  float *red = reinterpret_cast<float *>(sk_lds);
+  static_assert(kTile * 4 <= kSlot, "partials fit the first ring entry");
+  float *red = reinterpret_cast<float *>(sk_ring0);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < MT; ++u)
@@ -467,9 +473,9 @@ hipError_t run_skinny(const SkPlan &p, const float *X, const int32_t *qw, const 
                       float *Y, int M, int N, int G, hipStream_t stream) {
   const long blocks = long(p.tiles_m) * p.tiles_n;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_mx<MT, NT, kSkSG, kSkP>), dim3(unsigned(blocks)),
-                     dim3(64 * kSkWaves), size_t(sk_lds_bytes(MT, NT)), stream,
-                     X, reinterpret_cast<const uint32_t *>(qw), sc, Y, M, N, G, p.tiles_n);
+  hipLaunchKernelGGL((skinny_mx<MT, NT, kSkP>), dim3(unsigned(blocks)), dim3(64 * kSkWaves), 0,
+                     stream, X, reinterpret_cast<const uint32_t *>(qw), sc, Y, M, N, G,
+                     p.tiles_n);
   return hipGetLastError();
 }
 
