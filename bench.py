@@ -74,7 +74,7 @@ PATHS = ("auto", "gemv", "gemv-fma", "tile", "split", "packed", "swiglu", "repac
 # paths whose products are fp16 matrix instructions on two activation limbs
 LIMB_PATHS = ("split", "packed", "repacked", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
-PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
+PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common.h", "limbs.h"],
                 "gemv-fma": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],

@@ -332,17 +332,19 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
                                  codes (nibble - 8) and two fp16 limbs of each activation; every
                                  group of 32 activations is scaled by a power of two (max |x|
                                  into [2^14, 2^15)) before the split, so the limbs hold 22
-                                 significant bits; products exact in fp32, fp32 accumulation,
-                                 one fp32 multiply per (row, group) applies scale * 2^-e */
+                                 significant bits of every activation down to 2^-28 of its
+                                 group's maximum (the low limb carried x2^11); products exact
+                                 in fp32, fp32 accumulation, one fp32 multiply per (row,
+                                 group) applies scale * 2^-e */
 #define W4A16_GEMV_FMA 2      /* M <= 2 with K > 8192, or M > 64 forced onto the GEMV path:
                                  one fp32 FMA per weight, activations in VGPRs */
 #define W4A16_GEMV_SKINNY 3   /* 3 <= M <= 64 otherwise (the tree-verification batches):
                                  v_mfma_f32_16x16x32_f16 on exact weight codes and two fp16
                                  limbs of each activation, prescaled by a power of two per
-                                 row and step of 4 groups (2 with more than 16 rows), the low
-                                 limb x2^11 and met by the codes x2^-11; fp32 accumulation;
-                                 8 waves of a workgroup split K and add their partial tiles
-                                 in order; no workspace */
+                                 row and pair of groups, the low limb x2^11 and met by the
+                                 codes x2^-11; fp32 accumulation; 16 rows of X by 16-64 rows
+                                 of W per workgroup, whose 8 waves split K in steps of 4
+                                 groups and add their partial tiles in order; no workspace */
 
 /* The kernel W4A16_PATH_GEMV runs for an M x N x K shape (one of W4A16_GEMV_*), or 0
  * for a shape w4a16_gemm refuses.  Host only; no GPU use.  (Decode GEMV: the pages'
@@ -366,12 +368,23 @@ size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Y = X . dequant(qweight, scales)^T on the fp16 matrix cores with fp32
  * accumulation: each weight code (nibble - 8) is exact in fp16; each row of X is
  * scaled by a power of two (max |x| into [2^14, 2^15)) and split into two fp16
- * limbs whose sum holds 22 significant bits of every activation (relative error
- * <= 2^-23); the products are exact in fp32 and accumulated in fp32, one fp32
- * FMA per group applies the group scale, and the row's power of two is undone
- * exactly at the store.  A second kernel-side reading of the same operation
- * the pages define (fp32 activations, int4 weights, fp32 accumulation), for
- * compute-bound shapes.
+ * limbs hi = f16(x'), lo = f16(x' - hi); the products are exact in fp32 and
+ * accumulated in fp32, one fp32 FMA per group applies the group scale, and the
+ * row's power of two is undone exactly at the store.  A second kernel-side
+ * reading of the same operation the pages define (fp32 activations, int4
+ * weights, fp32 accumulation), for compute-bound shapes.
+ *
+ * Range: the limbs hold 22 significant bits of every activation down to about
+ * 2^-17 of its row's largest magnitude; smaller ones keep an absolute error
+ * below 2^-39 of that maximum (the low limb reaches the fp16 subnormals).  The
+ * tolerance of w4a16_gemm holds for rows whose magnitudes span up to about
+ * 2^22; a row spanning 2^26 or more whose largest entries meet zero weights
+ * can leave it.  The same holds for the other entry points on this arithmetic
+ * (w4a16_gemm_split_packed, w4a16_gemm_grouped(_packed), w4a16_gemm_repacked,
+ * w4a16_gemm_small_packed(_noalloc), the last per row and K slice).
+ * w4a16_gemm's own limb kernels (W4A16_GEMV_MFMA, W4A16_GEMV_SKINNY) take a
+ * power of two per row and one or two groups of 32 and carry the low limb
+ * x2^11, which keeps the tolerance for rows spanning 2^30 and more.
  *
  * `workspace` is a DEVICE buffer owned by the caller, 256-byte aligned, of at
  * least w4a16_split_workspace_bytes(M, N, K) bytes, not overlapping any other
