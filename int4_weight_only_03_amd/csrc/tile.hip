@@ -322,8 +322,17 @@ tile_lds(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;
-  const int bm = blockIdx.x / tiles_n;
-  const int bn = blockIdx.x - bm * tiles_n;
+#ifndef W4A16_TILE_XCD
+#define W4A16_TILE_XCD 1
+#endif
+  int tile = blockIdx.x;
+  if (W4A16_TILE_XCD && gridDim.x % 8 == 0) {
+    // the hardware deals workgroups round-robin to the 8 XCDs: XCD x takes
+    // the contiguous run of tiles x * (tiles / 8) ..
+    tile = int(blockIdx.x % 8) * int(gridDim.x / 8) + int(blockIdx.x / 8);
+  }
+  const int bm = tile / tiles_n;
+  const int bn = tile - bm * tiles_n;
   const int m0 = bm * 128, n0 = bn * 128;
   const int l32 = lane & 31;
   const int h = lane >> 5;
