@@ -161,13 +161,14 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
 /* Y[M][N] = X[M][K] . dequant(W)^T with W repacked by w4a16_repack(..., N, K,
  * ...).  No workspace and no allocation: for M <= 4 (when the activation limbs
  * fit the kernel's LDS) a decode GEMV whose workgroups split K over their
- * waves; otherwise one workgroup per 256 columns and 16 rows of X walks all
- * of K in slices of up to 32 groups and adds the slices in order.  Both run
- * on the fp16 matrix instructions with the arithmetic of w4a16_gemm_split
- * (exact weight codes, two fp16 limbs of each activation prescaled by a power
- * of two per row and K slice, fp32 accumulation; a row of X holding Inf or
- * NaN gives NaN in that row of Y) within the tolerance of w4a16_gemm, and
- * both are deterministic.  X (16-byte aligned), packed (16-byte aligned) and
+ * waves, with the arithmetic of w4a16_gemm_split (limbs prescaled per row);
+ * for M <= 64 otherwise the kernel of W4A16_GEMV_SKINNY reading the repacked
+ * blocks whole (limbs prescaled per row and pair of groups, low limb x2^11);
+ * above that one workgroup per 256 columns and 16 rows of X walks all of K
+ * in slices of up to 32 groups and adds the slices in order (limbs prescaled
+ * per row and K slice).  All on the fp16 matrix instructions with exact
+ * weight codes and fp32 accumulation (a row of X holding Inf or NaN gives NaN
+ * in that row of Y), within the tolerance of w4a16_gemm, and deterministic.  X (16-byte aligned), packed (16-byte aligned) and
  * Y (4-byte aligned) are DEVICE memory; Y must not overlap X or packed.
  * M == 0 or N == 0 is a no-op; otherwise errors as w4a16_gemm. */
 int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M, int64_t N,

@@ -101,7 +101,7 @@ __device__ __forceinline__ void sk_split2(float t0, float t1, float k, float m, 
       : "v"(t0), "v"(t1), "v"(k), "v"(m));
 }
 
-template <int MT, int NT, int P>
+template <int MT, int NT, int P, bool kRP>
 __global__ void __launch_bounds__(64 * kSkWaves)
 skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
           const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G,
@@ -169,6 +169,17 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   }
   const char *wtile = reinterpret_cast<const char *>(qw) + long(n0) * G * 16;
   const char *stile = reinterpret_cast<const char *>(sc) + long(n0) * G * 4;
+  // kRP: qw is w4a16_repack's buffer, a 1 KB block per (16-row tile, 4-group
+  // step) with lane l's 16 bytes its operand words for the 4 groups (word
+  // l / 16 of each, row l % 16), then a 256-byte block of the 16 rows' 4
+  // scales; the padding (rows to 16, groups to 4) holds weight and scale 0.
+  // Tiles past the last read the last one (never stored).
+  const int T16 = (N + 15) / 16, S4 = (G + SG - 1) / SG;
+  const char *pw = reinterpret_cast<const char *>(qw);
+  const char *ps = pw + long(T16) * S4 * 1024;
+  int ptile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ptile[t] = std::min(n0 / 16 + t, T16 - 1);
 
   // Step s's copies into slot v (kTail: the step past the whole steps, whose
   // groups past G re-read group G-1, masked later).  The offsets pass
@@ -180,10 +191,22 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
     const long gs = long(s) * SG;
 #pragma unroll
     for (int j = 0; j < kCopies; ++j) sk_opaque(xoff[j]);
+    if constexpr (!kRP) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      sk_opaque(woff[t]);
-      sk_opaque(soff[t]);
+      for (int t = 0; t < NT; ++t) {
+        sk_opaque(woff[t]);
+        sk_opaque(soff[t]);
+      }
+    } else {
+      // whole blocks of the repacked buffer, the partial last step included
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const long blk = long(ptile[t]) * S4 + s;
+        const char *wsrc = pw + blk * 1024 + 16 * lane;
+        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0, 0);
+        const char *ssrc = ps + blk * 256 + 4 * lane;
+        __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
+      }
     }
     if (!tail) {
       const char *xb = reinterpret_cast<const char *>(X) + gs * 128;
@@ -192,12 +215,15 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         const char *src = xb + xoff[j];
         __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + 1024 * j), 16, 0, 0);
       }
+      if constexpr (!kRP) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const char *wsrc = wtile + gs * 16 + woff[t];
-        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0, 0);
-        const char *ssrc = stile + gs * 4 + soff[t];
-        __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          const char *wsrc = wtile + gs * 16 + woff[t];
+          __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0,
+                                           0);
+          const char *ssrc = stile + gs * 4 + soff[t];
+          __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
+        }
       }
     } else {
       const char *xb = reinterpret_cast<const char *>(X);
@@ -209,13 +235,17 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
             xb + std::min(gs + q, long(G) - 1) * 128 + (xoff[j] - 128u * q);
         __builtin_amdgcn_global_load_lds(src, (sk_lds_void *)(slot + 1024 * j), 16, 0, 0);
       }
-      const long gw = std::min(gs + wg, long(G) - 1), gsc = std::min(gs + (lane & 3), long(G) - 1);
+      if constexpr (!kRP) {
+        const long gw = std::min(gs + wg, long(G) - 1);
+        const long gsc = std::min(gs + (lane & 3), long(G) - 1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const char *wsrc = wtile + gw * 16 + (woff[t] - 16u * uint32_t(wg));
-        __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0, 0);
-        const char *ssrc = stile + gsc * 4 + (soff[t] - 4u * uint32_t(lane & 3));
-        __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          const char *wsrc = wtile + gw * 16 + (woff[t] - 16u * uint32_t(wg));
+          __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0,
+                                           0);
+          const char *ssrc = stile + gsc * 4 + (soff[t] - 4u * uint32_t(lane & 3));
+          __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
+        }
       }
     }
   };
@@ -243,10 +273,18 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      if constexpr (kRP) {
+        const uint4 w4 = *reinterpret_cast<const uint4 *>(slot + kWOff + 1024 * t + 16 * lane);
+        o.w[t][0] = w4.x;
+        o.w[t][1] = w4.y;
+        o.w[t][2] = w4.z;
+        o.w[t][3] = w4.w;
+      } else {
 #pragma unroll
-      for (int g = 0; g < SG; ++g)
-        o.w[t][g] = *reinterpret_cast<const uint32_t *>(slot + kWOff + 1024 * t + 64 * c +
-                                                        16 * ((g + (c >> 2)) & 3) + 4 * R);
+        for (int g = 0; g < SG; ++g)
+          o.w[t][g] = *reinterpret_cast<const uint32_t *>(slot + kWOff + 1024 * t + 64 * c +
+                                                          16 * ((g + (c >> 2)) & 3) + 4 * R);
+      }
       o.sc[t] = *reinterpret_cast<const float4 *>(slot + kSOff + 256 * t + 16 * c);
     }
   };
@@ -468,15 +506,31 @@ SkPlan plan_skinny(int M, int N) {
   return p;
 }
 
-template <int MT, int NT>
-hipError_t run_skinny(const SkPlan &p, const float *X, const int32_t *qw, const float *sc,
+template <int MT, int NT, bool kRP>
+hipError_t run_skinny(const SkPlan &p, const float *X, const void *qw, const float *sc,
                       float *Y, int M, int N, int G, hipStream_t stream) {
   const long blocks = long(p.tiles_m) * p.tiles_n;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_mx<MT, NT, kSkP>), dim3(unsigned(blocks)), dim3(64 * kSkWaves), 0,
-                     stream, X, reinterpret_cast<const uint32_t *>(qw), sc, Y, M, N, G,
+  hipLaunchKernelGGL((skinny_mx<MT, NT, kSkP, kRP>), dim3(unsigned(blocks)), dim3(64 * kSkWaves),
+                     0, stream, X, reinterpret_cast<const uint32_t *>(qw), sc, Y, M, N, G,
                      p.tiles_n);
   return hipGetLastError();
+}
+
+template <bool kRP>
+hipError_t dispatch_skinny(const float *X, const void *qw, const float *sc, float *Y, int M,
+                           int N, int K, hipStream_t stream) {
+  if (!skinny_supported(M)) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  const SkPlan p = plan_skinny(M, N);
+#ifdef W4A16_SK_MT
+  if (p.MT == 2)
+    return p.NT == 1 ? run_skinny<2, 1, kRP>(p, X, qw, sc, Y, M, N, G, stream)
+                     : run_skinny<2, 2, kRP>(p, X, qw, sc, Y, M, N, G, stream);
+#endif
+  return p.NT == 1   ? run_skinny<1, 1, kRP>(p, X, qw, sc, Y, M, N, G, stream)
+         : p.NT == 2 ? run_skinny<1, 2, kRP>(p, X, qw, sc, Y, M, N, G, stream)
+                     : run_skinny<1, 4, kRP>(p, X, qw, sc, Y, M, N, G, stream);
 }
 
 }  // namespace
@@ -485,17 +539,12 @@ bool skinny_supported(int M) { return M >= 1 && M <= kSkinnyMaxM; }
 
 hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
                          int M, int N, int K, hipStream_t stream) {
-  if (!skinny_supported(M)) return hipErrorInvalidValue;
-  const int G = K / kGroup;
-  const SkPlan p = plan_skinny(M, N);
-#ifdef W4A16_SK_MT
-  if (p.MT == 2)
-    return p.NT == 1 ? run_skinny<2, 1>(p, X, qweight, scales, Y, M, N, G, stream)
-                     : run_skinny<2, 2>(p, X, qweight, scales, Y, M, N, G, stream);
-#endif
-  return p.NT == 1   ? run_skinny<1, 1>(p, X, qweight, scales, Y, M, N, G, stream)
-         : p.NT == 2 ? run_skinny<1, 2>(p, X, qweight, scales, Y, M, N, G, stream)
-                     : run_skinny<1, 4>(p, X, qweight, scales, Y, M, N, G, stream);
+  return dispatch_skinny<false>(X, qweight, scales, Y, M, N, K, stream);
+}
+
+hipError_t launch_skinny_repacked(const float *X, const void *packed, float *Y, int M, int N,
+                                  int K, hipStream_t stream) {
+  return dispatch_skinny<true>(X, packed, nullptr, Y, M, N, K, stream);
 }
 
 }  // namespace w4a16

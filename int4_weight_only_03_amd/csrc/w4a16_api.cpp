@@ -252,9 +252,13 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
   const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
-                     ? w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s)
-                     : w4a16::launch_small_packed_loop(X, packed, Y, int(M), int(N), int(K), s);
+  hipError_t e;
+  if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
+    e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
+  else if (w4a16::skinny_supported(int(M)))
+    e = w4a16::launch_skinny_repacked(X, packed, Y, int(M), int(N), int(K), s);
+  else
+    e = w4a16::launch_small_packed_loop(X, packed, Y, int(M), int(N), int(K), s);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

@@ -32,12 +32,15 @@ hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const
                                    float *Y, int M, int F, int K, hipStream_t stream);
 
 // Skinny GEMM (1 <= M <= kSkinnyMaxM) on the fp16 matrix instructions: exact
-// weight codes, two fp16 limbs of each activation prescaled per row and step
-// of 4 groups, fp32 accumulation; no workspace.
+// weight codes, two fp16 limbs of each activation prescaled per row and pair
+// of groups, fp32 accumulation; no workspace.
 constexpr int kSkinnyMaxM = 64;
 bool skinny_supported(int M);
 hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
                          int M, int N, int K, hipStream_t stream);
+// the skinny kernel on w4a16_repack's layout (one expert of the grouped pack)
+hipError_t launch_skinny_repacked(const float *X, const void *packed, float *Y, int M, int N,
+                                  int K, hipStream_t stream);
 
 // Tiled path: fp32 MFMA (32x32x2) on weight tiles dequantized into registers.
 hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
