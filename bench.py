@@ -80,7 +80,8 @@ PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
-                "repacked": ["packed_gemv.hip", "small_packed.hip", "gemv_common.h", "limbs.h"],
+                "repacked": ["packed_gemv.hip", "skinny.hip", "small_packed.hip", "gemv_common.h",
+                             "limbs.h"],
                 "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"],
                 "read-floor": ["read_floor.hip", "gemv_common.h"]}
 # launch shapes of the streaming-read floor: (threads per block, 16-byte loads per thread)
