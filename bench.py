@@ -18,11 +18,12 @@ path's arithmetic, otherwise that arithmetic's matrix peak), the
 streaming-read floor of the same bytes (a plain read of X, qweight and scales
 over the same rotating buffers, `w4a16_read_floor`, best of six launch
 shapes), the fp32-FMA GEMV beside the matrix-core GEMV for the M=1 decodes,
-and the other entry points for the two larger shapes (repacked, small-packed,
-split on packed weights; their one-time repack is timed apart).
+the fp32 tiled path beside the matrix-core tile for the prefill, and the other
+entry points for the two larger shapes (repacked, small-packed, split on
+packed weights; their one-time repack is timed apart).
 
 With --workload, one JSON line per (workload, path) instead (for profiling):
-paths auto, gemv, gemv-fma, tile, split, packed, swiglu, repacked,
+paths auto, gemv, gemv-fma, tile, tile-mx, split, packed, swiglu, repacked,
 small-packed, read-floor (the plain read of the same inputs, 256 threads x 4
 loads); grouped-MoE workloads take the public layout, or `packed` for the
 repacked grouped weights.
@@ -69,13 +70,14 @@ FLUSH_BYTES = 1 << 30
 SPIN_CYCLES = 1_000_000      # GPU clock cycles of the spin before the timed region
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "int4_weight_only_03_amd/csrc/"
-PATHS = ("auto", "gemv", "gemv-fma", "tile", "split", "packed", "swiglu", "repacked",
+PATHS = ("auto", "gemv", "gemv-fma", "tile", "tile-mx", "split", "packed", "swiglu", "repacked",
          "small-packed", "read-floor")
 # paths whose products are fp16 matrix instructions on two activation limbs
-LIMB_PATHS = ("split", "packed", "repacked", "small-packed")
+LIMB_PATHS = ("tile-mx", "split", "packed", "repacked", "small-packed")
 # the sources whose kernels a path runs (the C-ABI layer dispatches every path)
 PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common.h", "limbs.h"],
                 "gemv-fma": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
+                "tile-mx": ["tile_mx.hip", "limbs.h"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
@@ -279,7 +281,8 @@ class Problem:
                 pkg.w4a16_gemm_swiglu(x, q, s, y_out[i % C])
         else:
             code = {"auto": pkg.W4A16_PATH_AUTO, "gemv": pkg.W4A16_PATH_GEMV,
-                    "gemv-fma": pkg.W4A16_PATH_GEMV_FMA, "tile": pkg.W4A16_PATH_TILE}[path]
+                    "gemv-fma": pkg.W4A16_PATH_GEMV_FMA, "tile": pkg.W4A16_PATH_TILE,
+                    "tile-mx": pkg.W4A16_PATH_TILE_MX}[path]
 
             def step(i):
                 x, q, s, y = sets[i % C]
@@ -316,7 +319,7 @@ class Problem:
         if path != "auto":
             return path
         code = self.pkg.w4a16_select_path(self.wl.M, self.wl.N, self.wl.K)
-        return "gemv" if code == self.pkg.W4A16_PATH_GEMV else "tile"
+        return {self.pkg.W4A16_PATH_GEMV: "gemv", self.pkg.W4A16_PATH_TILE_MX: "tile-mx"}.get(code, "tile")
 
     def limb(self, resolved: str) -> bool:
         """Whether the path's products are fp16 matrix instructions on activation limbs."""
@@ -461,8 +464,8 @@ def headline(args) -> None:
                                                    "per_launch_event_us_median")}
         if name in ("verify_tree", "prefill"):
             alts = {}
-            others = ("small-packed", "repacked", "packed") if wl.M <= 64 else ("packed",
-                                                                                "repacked")
+            others = (("small-packed", "repacked", "packed") if wl.M <= 64
+                      else ("tile", "packed", "repacked"))
             for p in others:
                 a = prob.measure(p, steps, args.warmup)
                 a.pop("_y0")

@@ -84,6 +84,11 @@ extern "C" {
 #define W4A16_PATH_GEMV_FMA 4 /* the fp32 FMA GEMV kernels for any M and K: one fp32 FMA per
                                  weight with the activations in VGPRs (the GEMV path's kernel
                                  for K > 8192); for measurement beside the matrix-core GEMV */
+#define W4A16_PATH_TILE_MX 5  /* large-M matrix-core tile: fp16 MFMA 16x16x32 on exact (q - 8)
+                                 codes and two fp16 limbs of each activation, prescaled by a
+                                 power of two per row and pair of groups inside the kernel
+                                 (the skinny kernel's arithmetic); 128 x 128 tiles, no
+                                 workspace */
 
 /* Version of this ABI (W4A16_ABI_VERSION of the library that was built). */
 int w4a16_abi_version(void);
@@ -115,7 +120,7 @@ int w4a16_gemm(const float *X, const int32_t *qweight, const float *scales, floa
 
 /*
  * As w4a16_gemm, but with the kernel path forced (W4A16_PATH_AUTO, _GEMV,
- * _TILE or _GEMV_FMA; W4A16_PATH_SPLIT needs a workspace and is refused here
+ * _TILE, _GEMV_FMA or _TILE_MX; W4A16_PATH_SPLIT needs a workspace and is refused here
  * with W4A16_ERR_ARG).  Every path accepts every valid shape.  For tests and
  * measurement.
  */
@@ -354,8 +359,10 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
  * Knowledge".) */
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
 
-/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE): the GEMV
- * path for M <= 64, the tiled path otherwise. */
+/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV, _TILE_MX or _TILE):
+ * the GEMV path for M <= 64; above that the matrix-core tile when the shape has at
+ * least 96 tiles of 128 x 128 (ceil(M/128) * ceil(N/128) >= 96), the fp32 tiled
+ * path otherwise.  Host only; no GPU use. */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 
 /*

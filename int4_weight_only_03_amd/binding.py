@@ -25,6 +25,7 @@ W4A16_PATH_GEMV = 1
 W4A16_PATH_TILE = 2
 W4A16_PATH_SPLIT = 3
 W4A16_PATH_GEMV_FMA = 4
+W4A16_PATH_TILE_MX = 5
 
 _lib = None
 

@@ -1,6 +1,7 @@
-// Device helpers of the fp16 matrix-core kernels (split.hip, grouped.hip):
-// the power-of-two prescale and two-limb split of fp32 activations, and the
-// conversion of packed nibbles to exact fp16 weight codes (q - 8).
+// Device helpers of the fp16 matrix-core kernels (split, grouped, decode GEMV,
+// skinny and large-M tiles): the power-of-two prescale and two-limb split of
+// fp32 activations, and the conversion of packed nibbles to exact fp16 weight
+// codes (q - 8).
 //
 // Each activation row is scaled by 2^e so that its largest magnitude lies in
 // [2^14, 2^15), then split into hi = f16(x'), lo = f16(x' - hi), whose sum
@@ -81,6 +82,28 @@ __device__ __forceinline__ half8_t nibbles_to_f16(uint32_t w) {
   o[0] = r0[0]; o[1] = r0[1]; o[2] = r1[0]; o[3] = r1[1];
   o[4] = r2[0]; o[5] = r2[1]; o[6] = r3[0]; o[7] = r3[1];
   return o;
+}
+
+// max(|a|, |b|, |c|) in one instruction (fmaxf on loaded values costs a
+// canonicalising max per operand).  IEEE maxNum: a quiet NaN operand is
+// passed over.
+__device__ __forceinline__ float limb_absmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Limbs of two prescaled activations t0 = x0 2^(e+11), t1 = x1 2^(e+11) as
+// fp16 pairs (t0 in the low half): hi = f16(t 2^-11), lo = f16(t - 2^11 hi),
+// one mixed-precision FMA each, both rounded to nearest.  k = 2^-11, m = -2^11.
+__device__ __forceinline__ void limb_split2(float t0, float t1, float k, float m, uint32_t &hi,
+                                          uint32_t &lo) {
+  asm("v_fma_mixlo_f16 %0, %2, %4, 0\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0\n\t"
+      "v_fma_mixlo_f16 %1, %0, %5, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %0, %5, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(hi), "=&v"(lo)
+      : "v"(t0), "v"(t1), "v"(k), "v"(m));
 }
 
 }  // namespace

@@ -75,31 +75,9 @@ __device__ __forceinline__ void sk_wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | 0x70);
 }
 
-// max(|a|, |b|, |c|) in one instruction (fmaxf on loaded values costs a
-// canonicalising max per operand).  IEEE maxNum: a quiet NaN operand is
-// passed over.
-__device__ __forceinline__ float sk_absmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // An empty asm that claims to change x: keeps a loop-invariant offset's
 // uses (and their zero extension) inside the loop.
 __device__ __forceinline__ void sk_opaque(uint32_t &x) { asm volatile("" : "+v"(x)); }
-
-// Limbs of two prescaled activations t0 = x0 2^(e+11), t1 = x1 2^(e+11) as
-// fp16 pairs (t0 in the low half): hi = f16(t 2^-11), lo = f16(t - 2^11 hi),
-// one mixed-precision FMA each, both rounded to nearest.  k = 2^-11, m = -2^11.
-__device__ __forceinline__ void sk_split2(float t0, float t1, float k, float m, uint32_t &hi,
-                                          uint32_t &lo) {
-  asm("v_fma_mixlo_f16 %0, %2, %4, 0\n\t"
-      "v_fma_mixhi_f16 %0, %3, %4, 0\n\t"
-      "v_fma_mixlo_f16 %1, %0, %5, %2 op_sel_hi:[1,0,0]\n\t"
-      "v_fma_mixhi_f16 %1, %0, %5, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "=&v"(hi), "=&v"(lo)
-      : "v"(t0), "v"(t1), "v"(k), "v"(m));
-}
 
 template <int MT, int NT, int P, bool kRP>
 __global__ void __launch_bounds__(64 * kSkWaves)
@@ -321,20 +299,20 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
         const float4 a0 = xv[u][0][0], a1 = xv[u][0][1], a2 = xv[u][1][0], a3 = xv[u][1][1];
-        const float t0 = sk_absmax3(a0.x, a0.y, a0.z);
-        const float t1 = sk_absmax3(a0.w, a1.x, a1.y);
-        const float t2 = sk_absmax3(a1.z, a1.w, a2.x);
-        const float t3 = sk_absmax3(a2.y, a2.z, a2.w);
-        const float t4 = sk_absmax3(a3.x, a3.y, a3.z);
-        const float t5 = sk_absmax3(t0, t1, a3.w);
-        float mx = sk_absmax3(t2, t3, t4);
-        mx = sk_absmax3(mx, t5, 0.0f);
+        const float t0 = limb_absmax3(a0.x, a0.y, a0.z);
+        const float t1 = limb_absmax3(a0.w, a1.x, a1.y);
+        const float t2 = limb_absmax3(a1.z, a1.w, a2.x);
+        const float t3 = limb_absmax3(a2.y, a2.z, a2.w);
+        const float t4 = limb_absmax3(a3.x, a3.y, a3.z);
+        const float t5 = limb_absmax3(t0, t1, a3.w);
+        float mx = limb_absmax3(t2, t3, t4);
+        mx = limb_absmax3(mx, t5, 0.0f);
         const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                           false, false);
-        mx = sk_absmax3(__uint_as_float(h32[0]), __uint_as_float(h32[1]), 0.0f);
+        mx = limb_absmax3(__uint_as_float(h32[0]), __uint_as_float(h32[1]), 0.0f);
         const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                           false, false);
-        mx = sk_absmax3(__uint_as_float(h16[0]), __uint_as_float(h16[1]), 0.0f);
+        mx = limb_absmax3(__uint_as_float(h16[0]), __uint_as_float(h16[1]), 0.0f);
         // e in [-113, 116]: 2^-e and 2^(e+11) are normal fp32 numbers.  A
         // row whose pair maximum lies below 2^-102 keeps fewer limb bits; its
         // absolute error stays below 2^-120 of the weights' magnitude.
@@ -367,7 +345,7 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
           uint32_t hw[4], lw[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sk_split2(va[i] * up[u], vb[i] * up[u], 0x1p-11f, -2048.0f, hw[i], lw[i]);
+            limb_split2(va[i] * up[u], vb[i] * up[u], 0x1p-11f, -2048.0f, hw[i], lw[i]);
           hi[u] = __builtin_bit_cast(half8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
           lo[u] = __builtin_bit_cast(half8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }

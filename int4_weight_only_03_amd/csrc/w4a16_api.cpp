@@ -45,9 +45,11 @@ int validate_gemm(const float *X, const int32_t *qweight, const float *scales, f
   return W4A16_OK;
 }
 
-int select_path(int64_t M, int64_t K) {
+int select_path(int64_t M, int64_t N, int64_t K) {
   (void)K;
-  return M <= w4a16::kGemvMaxM ? W4A16_PATH_GEMV : W4A16_PATH_TILE;
+  if (M <= w4a16::kGemvMaxM) return W4A16_PATH_GEMV;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  return tiles >= w4a16::kTileMxMinTiles ? W4A16_PATH_TILE_MX : W4A16_PATH_TILE;
 }
 
 }  // namespace
@@ -70,19 +72,16 @@ const char *w4a16_status_str(int status) {
   }
 }
 
-int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  return select_path(M, K);
-}
+int w4a16_select_path(int64_t M, int64_t N, int64_t K) { return select_path(M, N, K); }
 
 int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales, float *Y,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, void *stream) {
   if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_TILE &&
-      path != W4A16_PATH_GEMV_FMA)
+      path != W4A16_PATH_GEMV_FMA && path != W4A16_PATH_TILE_MX)
     return W4A16_ERR_ARG;
   int st = validate_gemm(X, qweight, scales, Y, M, N, K, group);
   if (st != W4A16_OK || M == 0 || N == 0) return st;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K);
+  if (path == W4A16_PATH_AUTO) path = select_path(M, N, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   switch (path) {
@@ -91,6 +90,9 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
       break;
     case W4A16_PATH_GEMV_FMA:
       e = w4a16::launch_gemv_fma(X, qweight, scales, Y, int(M), int(N), int(K), s);
+      break;
+    case W4A16_PATH_TILE_MX:
+      e = w4a16::launch_tile_mx(X, qweight, scales, Y, int(M), int(N), int(K), s);
       break;
     default:
       e = w4a16::launch_tile(X, qweight, scales, Y, int(M), int(N), int(K), s);

@@ -45,6 +45,18 @@ hipError_t launch_skinny_repacked(const float *X, const void *packed, float *Y, 
 // Tiled path: fp32 MFMA (32x32x2) on weight tiles dequantized into registers.
 hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream);
+// Large-M matrix-core tile: fp16 MFMA on exact weight codes and two fp16 limbs
+// of each activation (prescaled per row and pair of groups inside the kernel);
+// 128 x 128 tiles, no workspace.
+long tile_mx_tiles(int M, int N);
+// w4a16_gemm takes the matrix-core tile above 64 rows from this many 128 x 128
+// tiles on: one workgroup per CU, so a launch of fewer tiles leaves CUs idle
+// for the whole of K, where the fp32 tiled path's smaller tiles and K splits
+// fill the chip (measured on MI355X: even at 56-64 tiles, the matrix-core tile
+// ahead from 96)
+constexpr long kTileMxMinTiles = 96;
+hipError_t launch_tile_mx(const float *X, const int32_t *qweight, const float *scales, float *Y,
+                          int M, int N, int K, hipStream_t stream);
 
 // Split-precision path: fp16 MFMA on exact weight codes and two fp16 limbs of
 // each activation; needs a caller workspace of split_workspace_bytes(M, N, K).

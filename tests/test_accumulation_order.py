@@ -19,6 +19,9 @@ from kernel code), with each product rounded to fp32 before it is added
 * matrix-core kernels (split path, grouped, small-M, decode GEMV on packed
   weights): each group's 32 products summed from zero, then one fp32 add of
   the group sum per group into the running total;
+* large-M matrix-core tile: each group's 32 products summed from zero, the two
+  group sums of a pair of groups added, then one fp32 add of the pair sum per
+  pair into the running total;
 * fp32 GEMV for long K: two chains of 16 products per group (even and odd k),
   their sum, then groups strided over 512 threads chained per thread, then the
   threads' partial sums added in order.
@@ -95,6 +98,22 @@ def group_chain_order(x, w):
     return acc
 
 
+def pair_chain_order(x, w):
+    P = (x * w).astype(f32)
+    O, K = P.shape
+    G = K // 32
+    acc = np.zeros(O, f32)
+    for g0 in range(0, G, 2):
+        pair = np.zeros(O, f32)
+        for g in range(g0, min(g0 + 2, G)):
+            d = np.zeros(O, f32)
+            for i in range(32):
+                d = (d + P[:, 32 * g + i]).astype(f32)
+            pair = (pair + d).astype(f32)
+        acc = (acc + pair).astype(f32)
+    return acc
+
+
 def gemv_long_order(x, w, threads=512):
     P = (x * w).astype(f32)
     O, K = P.shape
@@ -137,6 +156,12 @@ def test_unblocked_chain_fails_at_the_limit():
 def test_group_chain_stays_inside(K):
     x, w = coherent(K)
     assert ratio(group_chain_order(x, w), x, w) <= 0.5
+
+
+@pytest.mark.parametrize("K", [7168, K_MAX])
+def test_pair_chain_stays_inside(K):
+    x, w = coherent(K)
+    assert ratio(pair_chain_order(x, w), x, w) <= 0.5
 
 
 def test_long_k_gemv_stays_inside():

@@ -2,8 +2,9 @@
 
 * The prefill workload (M = 4096, K = 7168, N = 4096): every output of every
   path against one fp64 oracle product (computed once per module).
-* Ragged shapes that select the 128 x 128 tiled kernel (M > 64 with at least
-  512 such tiles): clamped edge reads and masked stores, every output.
+* Ragged shapes with many 128 x 128 tiles (what w4a16_gemm runs on the
+  matrix-core tile, and the fp32 tiled path's 128 x 128 kernel forced):
+  clamped edge reads and masked stores, every output.
 * Sign-coherent inputs (every activation >= 0 and every weight code >= 8, so
   no rounding error of a sum cancels) at K = 7168 and at the largest K each
   kernel takes, up to the library's K limit 2^17.
@@ -51,6 +52,8 @@ def run(X, qw, sc, path, dev):
         Y = binding.w4a16_gemm_path(Xd, Qd, Sd, path=binding.W4A16_PATH_GEMV)
     elif path == "tile":
         Y = binding.w4a16_gemm_path(Xd, Qd, Sd, path=binding.W4A16_PATH_TILE)
+    elif path == "tile-mx":
+        Y = binding.w4a16_gemm_path(Xd, Qd, Sd, path=binding.W4A16_PATH_TILE_MX)
     elif path == "split":
         Y = binding.w4a16_gemm_split(Xd, Qd, Sd)
     elif path == "packed":
@@ -89,22 +92,23 @@ def prefill():
     return Ref(*workloads.make("prefill"))
 
 
-@pytest.mark.parametrize("path", ["auto", "split", "packed", "repacked"])
+@pytest.mark.parametrize("path", ["auto", "tile", "split", "packed", "repacked"])
 def test_prefill_every_output(dev, prefill, path):
-    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE_MX
     say(f"prefill every output path={path}")
     prefill.check(run(prefill.X, prefill.qw, prefill.sc, path, dev), f"prefill {path}")
 
 
 @pytest.fixture(scope="module")
 def ragged_big():
-    # 33 x 32 = 1056 tiles of 128 x 128 (>= 512, M > 64): the 128 x 128 kernel,
-    # with a partial last row tile (4 rows) and column tile (32 columns)
+    # 33 x 32 = 1056 tiles of 128 x 128: the matrix-core tile (and, forced, the
+    # fp32 path's 128 x 128 kernel), with a partial last row tile (4 rows) and
+    # column tile (32 columns)
     say("ragged oracle (M=4100 K=7168 N=4000, fp64)")
     return Ref(*workloads.random_case(4100, 4000, 7168, seed=41))
 
 
-@pytest.mark.parametrize("path", ["auto", "split", "packed", "repacked"])
+@pytest.mark.parametrize("path", ["auto", "tile", "split", "packed", "repacked"])
 def test_ragged_wide_tiles_every_output(dev, ragged_big, path):
     say(f"ragged M=4100 N=4000 K=7168 path={path}")
     ragged_big.check(run(ragged_big.X, ragged_big.qw, ragged_big.sc, path, dev),
@@ -112,7 +116,7 @@ def test_ragged_wide_tiles_every_output(dev, ragged_big, path):
 
 
 @pytest.mark.parametrize("M,N,K", [(4100, 4000, 96), (4097, 4095, 32), (8191, 2049, 224)])
-@pytest.mark.parametrize("path", ["auto", "split", "repacked"])
+@pytest.mark.parametrize("path", ["auto", "tile", "split", "repacked"])
 def test_ragged_wide_tiles_short_k(dev, M, N, K, path):
     say(f"ragged M={M} N={N} K={K} path={path}")
     X, W = workloads.random_case(M, N, K, seed=M + N + K)
@@ -128,6 +132,7 @@ COHERENT = [
     (1, 64, K_MAX, ["auto", "split", "packed", "repacked", "small-packed"]),   # fp32 GEMV
     (2, 40, K_MAX, ["auto", "repacked"]),
     (9, 64, K_MAX, ["auto", "split", "repacked", "small-packed"]),             # skinny tiles
+    (130, 64, K_MAX, ["tile", "tile-mx"]),                                     # both tiles
 ]
 
 
@@ -142,10 +147,13 @@ def test_sign_coherent(dev, M, N, K, paths):
 
 
 def test_sign_coherent_wide_tiles(dev):
-    # the 128 x 128 kernel (32 x 16 tiles of 128) on coherent products over K = 16384
+    # 32 x 16 tiles of 128 on coherent products over K = 16384: the matrix-core
+    # tile, and the fp32 path's 128 x 128 kernel
     M, N, K = 4096, 2048, 16384
-    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE_MX
     X, W = workloads.coherent_case(M, N, K, seed=9)
     say("coherent wide-tile oracle (M=4096 K=16384 N=2048, fp64)")
     ref = Ref(X, W)
-    ref.check(run(X, ref.qw, ref.sc, "auto", dev), "coherent 4096x2048x16384 tile")
+    for path in ("auto", "tile"):
+        say(f"coherent 4096x2048x16384 path={path}")
+        ref.check(run(X, ref.qw, ref.sc, path, dev), f"coherent 4096x2048x16384 {path}")

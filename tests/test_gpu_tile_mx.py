@@ -1,0 +1,164 @@
+"""GPU parity of the large-M matrix-core tile (W4A16_PATH_TILE_MX: fp16 MFMA on
+exact weight codes and two activation limbs prescaled per row and pair of
+groups, 128 x 128 tiles), the kernel w4a16_gemm runs for M > 64 from 96 such
+tiles on, against the CPU oracle through the C ABI."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_only_03_amd import binding  # noqa: E402
+
+TMX = binding.W4A16_PATH_TILE_MX
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run(X, qw, sc, dev, Y=None, path=TMX):
+    out = binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev), Y, path=path)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(Y, X, qw, sc, what):
+    v = oracle.compare(Y, X, qw, sc)
+    say(f"{what}: max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], (what, v)
+
+
+# M: one row, a partial tile, one tile, a tile and a row, several; N likewise;
+# K: one group (a lone one-group pair), odd group counts (the last pair holds
+# one group), group counts not a multiple of the 4-group weight block, long K
+MS = [1, 65, 128, 129, 300]
+NK = [(1, 32), (17, 96), (130, 224), (257, 2080), (128, 1056), (300, 7168)]
+
+
+@pytest.mark.parametrize("M", MS)
+@pytest.mark.parametrize("N,K", NK)
+def test_shapes_against_oracle(dev, M, N, K):
+    say(f"tile-mx M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M * 7919 + N * 31 + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"tile-mx {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1000, 1030, 320), (1030, 1000, 96), (2048, 1024, 64)])
+def test_grids_with_and_without_the_xcd_order(dev, M, N, K):
+    # 8 x 9, 9 x 8 and 16 x 8 tiles: grids that are and are not multiples of 8
+    say(f"tile-mx grid M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M + 3 * N + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"tile-mx {M}x{N}x{K}")
+
+
+def test_auto_dispatch_reaches_it(dev):
+    M, N, K = 257, 4096, 256
+    assert binding.w4a16_select_path(M, N, K) == TMX
+    X, W = workloads.random_case(M, N, K, seed=5)
+    qw, sc = oracle.quantize(W)
+    Y = binding.w4a16_gemm(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev))
+    torch.cuda.synchronize()
+    a = Y.cpu().numpy()
+    check(a, X, qw, sc, "tile-mx auto 257x4096x256")
+    assert np.array_equal(a.view(np.uint32), run(X, qw, sc, dev).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 130, 512), (129, 64, 7168), (256, 256, 96)])
+def test_integer_inputs_exact(dev, M, N, K):
+    X, nib = workloads.integer_case(M, N, K, seed=K + N + M)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), dtype=np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+def test_deterministic_guard_band_and_scaling(dev):
+    M, N, K = 137, 145, 1056
+    X, W = workloads.random_case(M, N, K, seed=21)
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    a = run(X, qw, sc, dev, Y)
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    b = run(X, qw, sc, dev)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = run((X * np.float32(8.0)).astype(np.float32), qw, sc, dev)
+    assert np.array_equal(c, a * np.float32(8.0))
+    check(a, X, qw, sc, "tile-mx guarded")
+
+
+def test_pair_magnitudes_far_apart(dev):
+    # each pair of groups at its own power of two (2^-100 .. 2^100), zero
+    # pairs, fp32 subnormals, and a pair spanning 2^26 inside
+    rng = np.random.default_rng(12)
+    M, N, K = 140, 130, 4096
+    G = K // 32
+    X = rng.standard_normal((M, K))
+    exps = rng.integers(-100, 101, (M, G // 2))
+    X = X * np.repeat(np.exp2(exps.astype(np.float64)), 64, axis=1)
+    X[:, 64 * 3:64 * 4] = 0.0
+    X[0, 64 * 5:64 * 6] = rng.standard_normal(64) * 1e-42
+    X[1, 64 * 7:64 * 8] *= np.exp2(-rng.integers(0, 27, 64).astype(np.float64))
+    X = X.astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, "tile-mx magnitudes")
+
+
+def test_rows_spanning_2pow30_on_zero_weights(dev):
+    # one entry 2^30 times the row's scale, on a k whose weights are all zero:
+    # it sets its pair's exponent and adds nothing to sum |x w|
+    rng = np.random.default_rng(30)
+    M, N, K = 130, 96, 512
+    X = rng.standard_normal((M, K))
+    big = rng.integers(0, K, M)
+    X[np.arange(M), big] = 2.0 ** 30
+    W = rng.standard_normal((N, K)) * 0.02
+    W[:, np.unique(big)] = 0.0
+    X, W = X.astype(np.float32), W.astype(np.float32)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, "tile-mx 2^30 rows")
+
+
+def test_nonfinite_rows(dev):
+    M, N, K = 150, 40, 512
+    X, W = workloads.random_case(M, N, K, seed=13)
+    X[2, 7] = np.inf
+    X[140, 300] = np.nan
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, dev)
+    assert np.all(np.isnan(Y[2])) and np.all(np.isnan(Y[140]))
+    keep = [i for i in range(M) if i not in (2, 140)]
+    check(Y[keep], X[keep], qw, sc, "tile-mx finite rows")
+
+
+def test_same_as_fp32_tile_within_tolerance(dev):
+    # both tiled kernels on one problem; each inside the oracle's bound
+    X, W = workloads.random_case(384, 512, 2048, seed=8)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, "tile-mx 384x512x2048")
+    check(run(X, qw, sc, dev, path=binding.W4A16_PATH_TILE), X, qw, sc, "tile 384x512x2048")

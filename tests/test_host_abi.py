@@ -59,12 +59,18 @@ def test_gemv_kernel(lib):
 
 
 def test_select_path(lib):
-    # the decode/verify path for M <= 64, the tiled path above
+    # the decode/verify path for M <= 64; above, the matrix-core tile from 96
+    # tiles of 128 x 128 on, the fp32 tiled path below
     for M in (1, 4, 5, 8, 9, 17, 64):
         assert binding.w4a16_select_path(M, 4096, 7168) == binding.W4A16_PATH_GEMV
     assert binding.w4a16_select_path(5, 4096, 8192 + 32) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(65, 4096, 7168) == binding.W4A16_PATH_TILE
-    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE
+    assert binding.w4a16_select_path(65, 4096, 7168) == binding.W4A16_PATH_TILE      # 32 tiles
+    assert binding.w4a16_select_path(256, 4096, 7168) == binding.W4A16_PATH_TILE     # 64 tiles
+    assert binding.w4a16_select_path(257, 4096, 7168) == binding.W4A16_PATH_TILE_MX  # 96 tiles
+    assert binding.w4a16_select_path(65, 12161, 7168) == binding.W4A16_PATH_TILE_MX  # 96
+    assert binding.w4a16_select_path(65, 12160, 7168) == binding.W4A16_PATH_TILE     # 95
+    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE_MX
+    assert binding.w4a16_select_path(1 << 24, 1 << 30, 32) == binding.W4A16_PATH_TILE_MX
 
 
 # ------------------------------------------------------------------ quantize

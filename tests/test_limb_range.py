@@ -9,8 +9,9 @@ x' = x * 2^e, with the largest magnitude of some block of the row scaled into
   grouped GEMM, ``w4a16_gemm_repacked`` and ``w4a16_gemm_small_packed``) takes
   one exponent per row (per row and K slice on the small-M kernel) and keeps
   the low limb unscaled: hi = f16(x'), lo = f16(x' - hi);
-* the decode GEMV (one exponent per row and group of 32) and the skinny
-  kernel (per row and pair of groups) carry the low limb times 2^11:
+* the decode GEMV (one exponent per row and group of 32), the skinny kernel
+  and the large-M matrix-core tile (per row and pair of groups) carry the low
+  limb times 2^11:
   lo = f16((x' - hi) * 2^11), away from the fp16 subnormals.
 
 These tests emulate each representation in NumPy from that statement (no code
@@ -47,7 +48,8 @@ def rep_row_unscaled(x):
 
 def rep_block_scaled(x, block):
     """Exponent per row and block of `block` k, low limb carried x2^11 (the
-    decode GEMV with block 32, the skinny kernel with block 64)."""
+    decode GEMV with block 32, the skinny kernel and the large-M matrix-core
+    tile with block 64)."""
     x = np.asarray(x, np.float32).astype(np.float64)
     M, K = x.shape
     xb = x.reshape(M, K // block, block)
@@ -119,7 +121,7 @@ def test_split_family_limit_rows_spanning_2pow30():
 
 def test_block_exponent_paths_hold_rows_spanning_2pow30():
     """The same rows stay inside the tolerance with an exponent per group (the
-    decode GEMV) or per pair of groups (the skinny kernel)."""
+    decode GEMV) or per pair of groups (the skinny kernel, the large-M tile)."""
     X, qw, sc = far_apart_case(30)
     for block in (32, 64):
         assert worst_ratio(rep_block_scaled(X, block), X, qw, sc) < 0.5
