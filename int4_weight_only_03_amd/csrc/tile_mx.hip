@@ -20,18 +20,21 @@
 // (wm, wn) = (wave / 2, wave % 2) owns rows wm*32 .. +31 of X (2 row tiles u)
 // and rows wn*64 .. +63 of W (4 column tiles t).
 //
-// Pipeline, per pair of groups p (one s_barrier each):
-//   * the raw fp32 activations of pair p + 2 are copied into LDS (direct
-//     copies, 1 KB per instruction, each row's 16 chunks XOR-swizzled);
-//   * the workgroup splits pair p + 1 once (wave w takes rows 16w .. 16w+15:
-//     the pair's row maximum over 4 lanes, the exponent, the limbs) and writes
-//     the limbs and the factors 2^-e to LDS;
-//   * every wave reads pair p's limbs and factors, converts its W rows' codes
-//     and runs pair p's matrix instructions.
-// The split of pair p + 1 and the products of pair p are independent, so one
-// wave's conversions overlap its own matrix instructions.  Raw, limb, weight
-// and scale images alternate in pairs of separate __shared__ objects (so the
-// compiler can tell the reads of one from the copies into the other).
+// Pipeline, per pair of groups p (one s_barrier each).  Three LDS images each
+// hold one pair's 128 activation rows, first raw and then, split in place, as
+// limbs; two hold a pair's fp16 weight codes.  In iteration p every wave
+//   * issues the copies of pair p + 2's raw activations and scales (direct
+//     copies into the image pair p - 1 used) and loads pair p + 2's weight
+//     words (8 bytes per lane) into registers;
+//   * reads pair p's limbs, codes, scales and factors 2^-e, and pair p + 1's
+//     raw activations of its own 16 rows (copied by itself);
+//   * converts pair p + 1's weight words (loaded one pair earlier) into codes
+//     and splits pair p + 1 (the rows' pair maximum over 4 lanes, the
+//     exponent, the limbs, written over the raw values) while it runs pair
+//     p's matrix instructions.
+// Every copy and load of an iteration is waited for before the next one's
+// barrier, one iteration after it was issued.  Images are separate __shared__
+// objects.
 
 #include "w4a16_internal.h"
 #include "limbs.h"
@@ -51,6 +54,21 @@ __device__ __forceinline__ void lx_wait_vm0() {
 __device__ __forceinline__ void lx_wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | 0x70);  // lgkmcnt(0)
 }
+// Direct copy global -> LDS of 16 (or 4) bytes per lane: lane i writes at
+// lds + 16 i (4 i).  Written as asm so that the compiler does not track the
+// copies: it cannot tell their target images from the ones being read and
+// would wait for every copy in flight before each LDS access; the kernel's own
+// vmcnt waits order the copies.  The LDS address is wave-uniform (m0).
+__device__ __forceinline__ void lx_copy16(const void *src, const void *lds) {
+  const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((const lx_lds_void *)lds));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(a) : "memory", "m0");
+}
+__device__ __forceinline__ void lx_copy4(const void *src, const void *lds) {
+  const uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((const lx_lds_void *)lds));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(a) : "memory", "m0");
+}
 // Workgroup barrier without the release fence of __syncthreads() (which would
 // wait for the next pairs' copies as well).
 __device__ __forceinline__ void lx_barrier() {
@@ -62,22 +80,24 @@ __device__ __forceinline__ void lx_barrier() {
 __global__ void __launch_bounds__(64 * kLxWaves)
 tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G, int tiles_n) {
-  // raw activations of a pair: row r at 256 r, logical chunk L (k = 4L..4L+3
-  // of the pair) at physical chunk L ^ (r % 16)
-  __shared__ __align__(16) unsigned char lx_x0[128 * 256];
-  __shared__ __align__(16) unsigned char lx_x1[128 * 256];
-  // limbs of a pair: row r at 256 r, logical chunk 8 limb + 4 q + b (limb 0 =
-  // hi, 1 = lo; group q; k = 8b .. 8b+7 of the group, in the order the nibble
-  // conversion produces) at physical chunk (8 limb + 4 q + b) ^ (r % 16)
-  __shared__ __align__(16) unsigned char lx_l0[128 * 256];
-  __shared__ __align__(16) unsigned char lx_l1[128 * 256];
-  // weight words of 4 groups: row n at 64 n, group g at position g ^ ((n / 4) % 4)
-  __shared__ __align__(16) unsigned char lx_w0[128 * 64];
-  __shared__ __align__(16) unsigned char lx_w1[128 * 64];
-  // scales of 4 groups: row n at 16 n
-  __shared__ __align__(16) unsigned char lx_s0[128 * 16];
-  __shared__ __align__(16) unsigned char lx_s1[128 * 16];
-  // 2^-e of a pair, per row
+  // A pair's activations: row r at 256 r.  Raw: logical chunk L (k = 4L..4L+3
+  // of the pair) at physical chunk L ^ (r % 16).  Limbs: logical chunk
+  // 8 limb + 4 q + b (limb 0 = hi, 1 = lo; group q; k = 8b .. 8b+7 of the
+  // group, in the order the nibble conversion produces) at physical chunk
+  // (8 limb + 4 q + b) ^ (r % 16).  Pair p lives in image p % 3.
+  __shared__ __align__(16) unsigned char lx_a0[128 * 256];
+  __shared__ __align__(16) unsigned char lx_a1[128 * 256];
+  __shared__ __align__(16) unsigned char lx_a2[128 * 256];
+  // a pair's fp16 codes q - 8: W row n at 128 n, word R of group q (8 codes,
+  // in the nibble conversion's order) at chunk (4 q + R) ^ ((n / 2) % 8);
+  // pair p in image p % 2
+  __shared__ __align__(16) unsigned char lx_c0[128 * 128];
+  __shared__ __align__(16) unsigned char lx_c1[128 * 128];
+  // a pair's scales: row n at 8 n; pair p in image p % 3
+  __shared__ __align__(16) unsigned char lx_s0[128 * 8];
+  __shared__ __align__(16) unsigned char lx_s1[128 * 8];
+  __shared__ __align__(16) unsigned char lx_s2[128 * 8];
+  // 2^-e of a pair, per row; pair p in image p % 2
   __shared__ __align__(16) float lx_f0[128];
   __shared__ __align__(16) float lx_f1[128];
   const int lane = threadIdx.x & 63;
@@ -108,43 +128,49 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
     xoff[jj] = uint32_t(std::min(m0 + row, M - 1) - m0) * uint32_t(K * 4) + 16u * uint32_t(L);
   }
   const char *xtile = reinterpret_cast<const char *>(X) + long(m0) * K * 4;
-  // W copy (this wave issues copy `wave` of 8): lane i writes 16 B at offset
-  // 1024 wave + 16 i: tile row 16 wave + i/4, position i % 4, which holds group
-  // (i % 4) ^ ((row / 4) % 4) of the 4-group block.  Scale copy: lane i writes
-  // 4 B at offset 256 wave + 4 i: the scale of group i % 4 of the same row.
-  // Rows past N read row N-1.
-  const int wrow = 16 * wave + lane / 4;
-  const int wgr = (lane & 3) ^ ((wrow >> 2) & 3);
-  const long wrow_g = std::min(n0 + wrow, N - 1);
-  const char *wsrc0 = reinterpret_cast<const char *>(qw) + wrow_g * G * 16;
-  const char *ssrc0 = reinterpret_cast<const char *>(sc) + wrow_g * G * 4;
+  // Scale copy (waves 0-3): lane i of wave w writes 4 B at 256 w + 4 i: row
+  // 32 w + i/2, group i % 2 of the pair.  Rows past N read row N-1.
+  const int srow_c = 32 * (wave & 3) + lane / 2;
+  const char *ssrc0 = reinterpret_cast<const char *>(sc) + long(std::min(n0 + srow_c, N - 1)) * G * 4;
+  // Weight words: thread t loads 8 B of W row t / 4: words 2 (t % 4) and
+  // 2 (t % 4) + 1 of the pair (group (t % 4) / 2, words R = 2 (t % 2), +1).
+  const int tid = int(threadIdx.x);
+  const int cn = tid >> 2, ch = tid & 3, cq = ch >> 1;
+  const char *wsrc0 = reinterpret_cast<const char *>(qw) + long(std::min(n0 + cn, N - 1)) * G * 16 + 8 * ch;
+  uint32_t cwrite[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cwrite[i] = uint32_t(cn * 128 + 16 * ((2 * ch + i) ^ ((cn >> 1) & 7)));
 
-  // pair p's raw activations (an odd G's last pair: its second group's chunks
-  // re-read the first group; their products meet a zero scale)
-  auto load_x = [&](unsigned char *img, int p) {
+  // pair p's raw activations and scales (an odd G's last pair: its second
+  // group's chunks re-read the first group; their products meet a zero scale)
+  auto copy_pair = [&](unsigned char *img, unsigned char *simg, int p) {
     const char *base = xtile + long(p) * 256;
     const bool one = 2 * p + 1 >= G;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint32_t o = xoff[jj] - ((one && xhigh[jj]) ? 128u : 0u);
-      const char *src = base + o;
-      __builtin_amdgcn_global_load_lds(src, (lx_lds_void *)(img + 1024 * (4 * wave + jj)), 16, 0, 0);
+      lx_copy16(base + o, img + 1024 * (4 * wave + jj));
+    }
+    if (wave < 4) {
+      const int g = std::min(2 * p + (lane & 1), G - 1);
+      lx_copy4(ssrc0 + long(g) * 4, simg + 256 * wave);
     }
   };
-  // the weights and scales of groups 4 blk .. 4 blk + 3 (groups past G re-read
-  // group G-1; never used)
-  auto load_ws = [&](unsigned char *wimg, unsigned char *simg, int blk) {
-    const long gw = std::min(4L * blk + wgr, long(G) - 1);
-    const long gs = std::min(4L * blk + (lane & 3), long(G) - 1);
-    const char *wsrc = wsrc0 + gw * 16;
-    __builtin_amdgcn_global_load_lds(wsrc, (lx_lds_void *)(wimg + 1024 * wave), 16, 0, 0);
-    const char *ssrc = ssrc0 + gs * 4;
-    __builtin_amdgcn_global_load_lds(ssrc, (lx_lds_void *)(simg + 256 * wave), 4, 0, 0);
+  auto load_w = [&](int p) -> uint2 {
+    const long off = long(p) * 32 - ((2 * p + 1 >= G && cq) ? 16 : 0);
+    return *reinterpret_cast<const uint2 *>(wsrc0 + off);
+  };
+  auto convert_w = [&](uint2 w, unsigned char *cimg) {
+    const half8_t b0 = nibbles_to_f16(w.x), b1 = nibbles_to_f16(w.y);
+    *reinterpret_cast<half8_t *>(cimg + cwrite[0]) = b0;
+    *reinterpret_cast<half8_t *>(cimg + cwrite[1]) = b1;
   };
 
   // Split: lane (c, R) of wave w takes row 16w + c, logical chunks 4R .. 4R+3
   // (k = 16R .. 16R+15 of the pair: group R / 2, 8-blocks 2 (R % 2) and
-  // 2 (R % 2) + 1 of it).
+  // 2 (R % 2) + 1 of it).  Every lane of a row has read its raw chunks before
+  // any writes limbs (the row maximum needs all four), and no other wave
+  // touches the row, so the limbs can replace the raw values.
   const int srow = 16 * wave + c;
   uint32_t sread[4];
 #pragma unroll
@@ -154,10 +180,11 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   for (int l = 0; l < 2; ++l)
 #pragma unroll
     for (int b = 0; b < 2; ++b) swrite[l][b] = uint32_t(srow * 256 + 16 * ((8 * l + 2 * R + b) ^ c));
-  auto split = [&](const unsigned char *ximg, unsigned char *limg, float *fimg) {
-    float4 v[4];
+  auto split_read = [&](const unsigned char *img, float4 (&v)[4]) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const float4 *>(ximg + sread[h]);
+    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const float4 *>(img + sread[h]);
+  };
+  auto split_write = [&](const float4 (&v)[4], unsigned char *img, float *fimg) {
     // the row's largest magnitude in the pair: over this lane's 16 values,
     // then over the row's 4 lanes (a NaN is passed over and still turns the
     // row's products to NaN)
@@ -188,25 +215,56 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         limb_split2(va[i] * up, vb[i] * up, 0x1p-11f, -2048.0f, hw[i], lw[i]);
-      *reinterpret_cast<uint4 *>(limg + swrite[0][b]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4 *>(limg + swrite[1][b]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4 *>(img + swrite[0][b]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(img + swrite[1][b]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
   };
 
   // Products: limbs of row wm*32 + 16u + c, group q, block R at
-  // lread[limb][q] + 4096 u; W word R of group g of row wn*64 + 16t + c at
-  // wread[g] + 1024 t; its scale at sread0 + 256 t + 4 g.
+  // lread[limb][q] + 4096 u; codes of W row wn*64 + 16t + c, word R of group
+  // q at cread[q] + 2048 t; its scale at sread0 + 128 t + 4 q; the factors of
+  // result rows wm*32 + 16u + 4R .. +3 at fread + 64 u.
   uint32_t lread[2][2];
 #pragma unroll
   for (int l = 0; l < 2; ++l)
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       lread[l][q] = uint32_t((wm * 32 + c) * 256 + 16 * ((8 * l + 4 * q + R) ^ c));
-  uint32_t wread[4];
+  uint32_t cread[2];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) wread[g] = uint32_t((wn * 64 + c) * 64 + 16 * (g ^ ((c >> 2) & 3)) + 4 * R);
-  const uint32_t sread0 = uint32_t((wn * 64 + c) * 16);
+  for (int q = 0; q < 2; ++q) {
+    const int n = wn * 64 + c;
+    cread[q] = uint32_t(n * 128 + 16 * ((4 * q + R) ^ ((n >> 1) & 7)));
+  }
+  const uint32_t sread0 = uint32_t((wn * 64 + c) * 8);
   const uint32_t fread = uint32_t((wm * 32 + 4 * R) * 4);
+
+  struct Ops {
+    half8_t hi[2][2], lo[2][2];  // [q][u]
+    half8_t b[2][4];             // [q][t]
+    float s[2][4];
+    float4 fac[2];
+  };
+  auto products_read = [&](const unsigned char *img, const unsigned char *cimg,
+                           const unsigned char *simg, const float *fimg, Ops &o) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        o.hi[q][u] = *reinterpret_cast<const half8_t *>(img + lread[0][q] + 4096 * u);
+        o.lo[q][u] = *reinterpret_cast<const half8_t *>(img + lread[1][q] + 4096 * u);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        o.b[q][t] = *reinterpret_cast<const half8_t *>(cimg + cread[q] + 2048 * t);
+        o.s[q][t] = *reinterpret_cast<const float *>(simg + sread0 + 128 * t + 4 * q);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      o.fac[u] = *reinterpret_cast<const float4 *>(
+          reinterpret_cast<const unsigned char *>(fimg) + fread + 64 * u);
+  };
 
   float acc[2][4][4];
 #pragma unroll
@@ -216,33 +274,21 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[u][t][r] = 0.0f;
 
-  // pair p from its limb, factor, weight and scale images; gq0 = 2 (p % 2),
-  // the pair's first group within the weight block
-  auto products = [&](const unsigned char *limg, const float *fimg, const unsigned char *wimg,
-                      const unsigned char *simg, int gq0, bool two) {
+  auto products = [&](const Ops &o, bool two) {
     float ss[2][4][4];  // the pair's sum, group scales applied, 2^-e not yet
     const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int gq = gq0 + q;
-      half8_t hi[2], lo[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        hi[u] = *reinterpret_cast<const half8_t *>(limg + lread[0][q] + 4096 * u);
-        lo[u] = *reinterpret_cast<const half8_t *>(limg + lread[1][q] + 4096 * u);
-      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(wimg + wread[gq] + 1024 * t);
-        const float s = *reinterpret_cast<const float *>(simg + sread0 + 256 * t + 4 * gq);
-        const float sq = (q == 0 || two) ? s : 0.0f;
-        const half8_t b = nibbles_to_f16(w);
+        const float sq = (q == 0 || two) ? o.s[q][t] : 0.0f;
+        const half8_t b = o.b[q][t];
         const _Float16 k2 = (_Float16)0x1p-11f;
         const half8_t b2 = b * half8_t{k2, k2, k2, k2, k2, k2, k2, k2};  // exact in fp16
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[u], b, zero, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[u], b2, d, 0, 0, 0);
+          floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.hi[q][u], b, zero, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.lo[q][u], b2, d, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) ss[u][t][r] = q == 0 ? sq * d[r] : fmaf(sq, d[r], ss[u][t][r]);
         }
@@ -250,10 +296,7 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // 2^-e of this lane's result rows wm*32 + 16u + 4R .. +3
-      const float4 fac = *reinterpret_cast<const float4 *>(
-          reinterpret_cast<const unsigned char *>(fimg) + fread + 64 * u);
-      const float f[4] = {fac.x, fac.y, fac.z, fac.w};
+      const float f[4] = {o.fac[u].x, o.fac[u].y, o.fac[u].z, o.fac[u].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -261,43 +304,61 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
     }
   };
 
-  // prologue: pairs 0 and 1 copied, the first weight block, pair 0 split
-  load_x(lx_x0, 0);
-  if (P > 1) load_x(lx_x1, 1);
-  load_ws(lx_w0, lx_s0, 0);
+  // prologue: pairs 0 and 1 copied and their weight words loaded; pair 0's
+  // codes converted and its activations split
+  copy_pair(lx_a0, lx_s0, 0);
+  uint2 wnext = load_w(0);
+  uint2 wlater = wnext;
+  if (P > 1) {
+    copy_pair(lx_a1, lx_s1, 1);
+    wlater = load_w(1);
+  }
   lx_wait_vm0();
-  lx_barrier();
-  split(lx_x0, lx_l0, lx_f0);
-  // Four pairs per iteration: raw, limb and factor images alternate per pair,
-  // weight and scale images per two pairs (4 groups).
-  for (int pb = 0; pb < P; pb += 4) {
+  {
+    float4 v[4];
+    split_read(lx_a0, v);  // this wave's own copies
+    convert_w(wnext, lx_c0);
+    split_write(v, lx_a0, lx_f0);
+  }
+  wnext = wlater;
+  // Six pairs per iteration (activation and scale images by p % 3, codes and
+  // factors by p % 2).
+  for (int pb = 0; pb < P; pb += 6) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < 6; ++v) {
       const int p = pb + v;
       if (p < P) {
-        unsigned char *xcur = (v & 1) ? lx_x1 : lx_x0;      // pair p + 2 lands here
-        unsigned char *xnext = (v & 1) ? lx_x0 : lx_x1;     // pair p + 1
-        unsigned char *lcur = (v & 1) ? lx_l1 : lx_l0;
-        unsigned char *lnext = (v & 1) ? lx_l0 : lx_l1;
+        const int i3 = v % 3;
+        unsigned char *acur = i3 == 0 ? lx_a0 : i3 == 1 ? lx_a1 : lx_a2;
+        unsigned char *anext = i3 == 0 ? lx_a1 : i3 == 1 ? lx_a2 : lx_a0;
+        unsigned char *afree = i3 == 0 ? lx_a2 : i3 == 1 ? lx_a0 : lx_a1;
+        unsigned char *scur = i3 == 0 ? lx_s0 : i3 == 1 ? lx_s1 : lx_s2;
+        unsigned char *sfree = i3 == 0 ? lx_s2 : i3 == 1 ? lx_s0 : lx_s1;
+        unsigned char *ccur = (v & 1) ? lx_c1 : lx_c0;
+        unsigned char *cnext = (v & 1) ? lx_c0 : lx_c1;
         float *fcur = (v & 1) ? lx_f1 : lx_f0;
         float *fnext = (v & 1) ? lx_f0 : lx_f1;
-        unsigned char *wcur = (v & 2) ? lx_w1 : lx_w0;
-        unsigned char *scur = (v & 2) ? lx_s1 : lx_s0;
-        unsigned char *wnext = (v & 2) ? lx_w0 : lx_w1;
-        unsigned char *snext = (v & 2) ? lx_s0 : lx_s1;
-        // After the barrier: pair p + 1's copies have landed and pair p's
-        // limbs are written (every wave waited for its own), and every wave is
-        // past pair p - 1 (whose images the copies and limbs below replace).
+        // Every copy and load issued one pair ago has landed (pair p + 1's
+        // activations, scales and weight words); after the barrier every
+        // wave's have, pair p's limbs and codes are written, and every wave
+        // is past pair p - 1 (whose images are reused below).
         asm volatile("" ::: "memory");
         lx_wait_vm0();
         lx_wait_lgkm0();
         lx_barrier();
-        // (the limbs are written before the next copies are issued: the
-        // compiler waits for every copy in flight before an LDS write)
-        if (p + 1 < P) split(xnext, lnext, fnext);
-        if (p + 2 < P) load_x(xcur, p + 2);
-        if ((v & 1) == 0 && 4 * (p / 2 + 1) < G) load_ws(wnext, snext, p / 2 + 1);
-        products(lcur, fcur, wcur, scur, 2 * (v & 1), 2 * p + 1 < G);
+        const uint2 wcur = wnext;  // pair p + 1's weight words
+        if (p + 2 < P) {
+          copy_pair(afree, sfree, p + 2);
+          wnext = load_w(p + 2);
+        }
+        Ops o;
+        products_read(acur, ccur, scur, fcur, o);
+        const bool more = p + 1 < P;
+        float4 xv[4];
+        if (more) split_read(anext, xv);
+        if (more) convert_w(wcur, cnext);
+        products(o, 2 * p + 1 < G);
+        if (more) split_write(xv, anext, fnext);
       }
     }
   }
