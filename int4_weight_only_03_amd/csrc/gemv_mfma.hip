@@ -12,12 +12,14 @@
 //
 // Arithmetic (the split path's, per group instead of per row):
 //  * Each group of 32 activations is scaled by 2^e so that its largest
-//    magnitude lies in [2^14, 2^15), and split into fp16 limbs hi = f16(x'),
-//    lo = f16((x' - hi) * 2^11); x' = hi + 2^-11 lo to 22 significant bits
-//    for every activation down to 2^-28 of the group maximum, and to an
-//    absolute 2^-50 of that maximum below it (lo carries 2^11 so that it
-//    stays out of the fp16 subnormals).  Products of a limb and an exact
-//    fp16 weight code (q - 8) are exact in fp32.
+//    magnitude lies in [2^14, 2^15) (e at most 116, so that 2^(e+11) is a
+//    normal fp32 number; only groups below 2^-101 are scaled less), and split
+//    into fp16 limbs hi = f16(x'), lo = f16((x' - hi) * 2^11), from
+//    t = x * 2^(e+11) with one mixed-precision FMA each; x' = hi + 2^-11 lo
+//    to 22 significant bits for every activation down to 2^-28 of the group
+//    maximum, and to an absolute 2^-50 of that maximum below it (lo carries
+//    2^11 so that it stays out of the fp16 subnormals).  Products of a limb
+//    and an exact fp16 weight code (q - 8) are exact in fp32.
 //  * v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products.  Block b
 //    of a wave is group g = 16*wave + b.  Its A operand (4 x 4) holds the limb
 //    rows (hi and lo of two activation rows; M = 3..8 take up to four A
@@ -38,8 +40,12 @@
 //
 // Loads: each lane first loads its 8 activations (the group's quarter j) and
 // then all of its weight and scale loads, so the weights stream while the
-// activations are split.  One workgroup covers 4R rows and all groups (one
-// wave per 16 groups, K <= 8192), about one workgroup per compute unit.
+// activations are split.  All are buffer loads whose resources end at the
+// last valid byte (the activation row at K, the workgroup's weights and
+// scales at row N): rows past N and groups past K read zero, with no clamped
+// addresses or selects, and each load's address is one 32-bit offset.  One
+// workgroup covers 4R rows and all groups (one wave per 16 groups,
+// K <= 8192), about one workgroup per compute unit.
 
 #include "w4a16_internal.h"
 #include "gemv_common.h"
@@ -53,6 +59,8 @@ namespace {
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMxMaxGroups = 256;  // 16 waves of 16 groups: K <= 8192
+// word 3 of a raw buffer resource (32-bit data format, no swizzle)
+constexpr int kRsrcWord3 = 0x00020000;
 
 // LDS: per wave [16 groups][limb rows of one A operand][4 quarters] of 8 fp16:
 // 2 limb rows for MT = 1 (2 KB), 4 otherwise (4 KB); with MT > 2 the A
@@ -75,33 +83,47 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
   constexpr int RL = kSw ? 2 * R : R;  // row quads per lane (gate quads, then up quads)
   constexpr int MS = (MT + 1) / 2;     // A operands of 4 limb rows (2 activation rows each)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int b = lane >> 2, j = lane & 3;
   const int g = wave * 16 + b;
   const bool gv = g < G;
-  const int gc = gv ? g : G - 1;  // clamped: every load stays in bounds
 
-  // activations first (quarter j of group gc of each row), then the weights
-  float4 xa[MT][2];
+  // Buffer loads: a workgroup's weight rows start its buffers, which end at
+  // row N (or at its last row), so rows past N read zero; a lane past the last
+  // group (g >= G) reads zero too (its offsets lie past every buffer).  The
+  // activation rows' buffers end at K: those lanes' activations are zero.
+  const uint32_t K4 = uint32_t(G) * kGroup * 4;
+  u32x4 xw[MT][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const float4 *xp = reinterpret_cast<const float4 *>(xr[m] + long(gc) * kGroup + 8 * j);
-    xa[m][0] = xp[0];
-    xa[m][1] = xp[1];
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(xr[m]), (short)0, int(K4), kRsrcWord3);
+    const uint32_t vx = uint32_t(g) * (kGroup * 4) + 32u * uint32_t(j);
+    xw[m][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, vx, 0, 0);
+    xw[m][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, vx + 16, 0, 0);
   }
   uint4 w[RL];
   float s[RL];
   {
-    // block-relative 32-bit offsets; rows past N read the last row (of their half)
-    const uint4 *qb = qw + rowbase * G;
-    const float *sb = sc + rowbase * G;
-    const int nmax = int(std::min(long(N) - 1 - rowbase, long(4 * R - 1)));
-    const long up = long(N) * G;  // kSw: the up half starts N rows further
+    const int rows = int(std::min(long(N) - rowbase, long(4 * R)));
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4 *>(qw + rowbase * G), (short)0, rows * G * 16, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(sc + rowbase * G), (short)0, rows * G * 4, kRsrcWord3);
+    __amdgpu_buffer_rsrc_t rwu = rw, rsu = rs;
+    if constexpr (kSw) {
+      rwu = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(qw + (long(N) + rowbase) * G),
+                                              (short)0, rows * G * 16, kRsrcWord3);
+      rsu = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(sc + (long(N) + rowbase) * G),
+                                              (short)0, rows * G * 4, kRsrcWord3);
+    }
+    const uint32_t e0 = gv ? uint32_t(j * G + g) : 0x08000000u;  // element offset of row j
 #pragma unroll
     for (int q = 0; q < RL; ++q) {
-      const int off = std::min(4 * (q % R) + j, nmax) * G + gc;
-      w[q] = load_stream16(qb + off + (q >= R ? up : 0));
-      s[q] = load_stream4(sb + off + (q >= R ? up : 0));
+      const uint32_t eq = e0 + uint32_t(4 * (q % R) * G);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(q >= R ? rwu : rw, eq * 16, 0, 2);
+      w[q] = make_uint4(v.x, v.y, v.z, v.w);
+      s[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q >= R ? rsu : rs, eq * 4, 0, 2));
     }
   }
 
@@ -121,26 +143,27 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
     for (int hh = 0; hh < 2; ++hh) {
       const int m = 2 * p + hh;
       if (m >= MT) break;
-      if (!gv) xa[m][0] = xa[m][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 a0 = xa[m][0], a1 = xa[m][1];
-      // maximum magnitude as an unsigned compare of the sign-cleared bits (same
-      // order as the magnitudes; a NaN compares above every finite value)
-      uint32_t mb = std::max(std::max(std::max(__float_as_uint(a0.x) & 0x7fffffffu, __float_as_uint(a0.y) & 0x7fffffffu),
-                                      std::max(__float_as_uint(a0.z) & 0x7fffffffu, __float_as_uint(a0.w) & 0x7fffffffu)),
-                             std::max(std::max(__float_as_uint(a1.x) & 0x7fffffffu, __float_as_uint(a1.y) & 0x7fffffffu),
-                                      std::max(__float_as_uint(a1.z) & 0x7fffffffu, __float_as_uint(a1.w) & 0x7fffffffu)));
-      // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad gets the group maximum
-      mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0xB1, 0xf, 0xf, false)));
-      mb = std::max(mb, uint32_t(__builtin_amdgcn_mov_dpp(int(mb), 0x4E, 0xf, 0xf, false)));
-      const float mx = __uint_as_float(mb);
-      // e in [-113, 126]: 2^-e is a normal fp32 number.  Groups below 2^-112
-      // keep fewer limb bits; their absolute error stays below 2^-130.
-      const int e = std::min(row_exponent(mx), 126);
+      const float v[8] = {__uint_as_float(xw[m][0].x), __uint_as_float(xw[m][0].y),
+                          __uint_as_float(xw[m][0].z), __uint_as_float(xw[m][0].w),
+                          __uint_as_float(xw[m][1].x), __uint_as_float(xw[m][1].y),
+                          __uint_as_float(xw[m][1].z), __uint_as_float(xw[m][1].w)};
+      // the group's largest magnitude (a NaN is passed over and still turns
+      // the row's products to NaN)
+      const float t0 = limb_absmax3(v[0], v[1], v[2]);
+      const float t1 = limb_absmax3(v[3], v[4], v[5]);
+      float mx = limb_absmax3(v[6], v[7], t0);
+      mx = limb_absmax3(mx, t1, 0.0f);
+      mx = limb_absmax3(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xf, 0xf, false)), 0.0f);
+      mx = limb_absmax3(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xf, 0xf, false)), 0.0f);
+      // e in [-113, 116]: 2^-e and 2^(e+11) are normal, x * 2^(e+11) exact
+      const int e = std::min(row_exponent(mx), 116);
       inv[m] = __int_as_float((127 - e) << 23);
-      half8_t h, l;
-      split_block_wide(a0, a1, e, h, l);
-      lb[(b * LR + 2 * hh) * 4 + j] = h;
-      lb[(b * LR + 2 * hh + 1) * 4 + j] = l;
+      const float up = __int_as_float((127 + e + 11) << 23);
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) limb_split2(v[i] * up, v[4 + i] * up, 0x1p-11f, -2048.0f, hw[i], lw[i]);
+      lb[(b * LR + 2 * hh) * 4 + j] = __builtin_bit_cast(half8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      lb[(b * LR + 2 * hh + 1) * 4 + j] = __builtin_bit_cast(half8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -174,7 +197,7 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
       for (int h = 0; h < 2; ++h) {
         const int m = 2 * p + h;
         if (m < MT) {
-          const float sp = gv ? s[q] * inv[m] : 0.0f;  // exact: a power-of-two factor
+          const float sp = s[q] * inv[m];  // exact: a power-of-two factor
           acc[m][q] = sp * fmaf(d[p][2 * h + 1], 0x1p-11f, d[p][2 * h]);
         }
       }

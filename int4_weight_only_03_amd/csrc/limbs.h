@@ -45,24 +45,6 @@ __device__ __forceinline__ void split_block(const float4 a, const float4 c, int 
   }
 }
 
-// Limbs of 8 activations a = x[k..k+3], c = x[k+4..k+7] with the low limb
-// carried x2^11 (out of the fp16 subnormals), in the order the nibble
-// conversion produces (x0 x4 x1 x5 x2 x6 x3 x7):
-// hi = f16(x * 2^e), lo = f16(x * 2^(e+11) - 2^11 * hi)  (= f16((x * 2^e - hi) * 2^11);
-// both products by powers of two and the difference are exact in fp32).
-// Every activation down to 2^-28 of the block maximum keeps 22 significant
-// bits when that maximum is scaled into [2^14, 2^15).
-__device__ __forceinline__ void split_block_wide(const float4 a, const float4 c, int e, half8_t &h,
-                                                 half8_t &l) {
-  const float v[8] = {a.x, c.x, a.y, c.y, a.z, c.z, a.w, c.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const _Float16 hv = (_Float16)ldexpf(v[i], e);
-    h[i] = hv;
-    l[i] = (_Float16)__builtin_fmaf((float)hv, -2048.0f, ldexpf(v[i], e + 11));
-  }
-}
-
 // f16 (q - 8) pairs from one word of 8 nibbles: VGPR p holds nibbles p, p+4.
 // (w & mask) | 0x6400 puts a nibble into the mantissa of 1024 (v_bitop3).
 __device__ __forceinline__ half8_t nibbles_to_f16(uint32_t w) {

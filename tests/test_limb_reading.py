@@ -21,13 +21,14 @@ import workloads
 
 
 def group_exponent(mx):
-    """e with mx * 2^e in [2^14, 2^15); 0 for zero or non-finite; at most 126."""
+    """e with mx * 2^e in [2^14, 2^15); 0 for zero or non-finite; at most 116
+    (the kernel forms 2^(e+11) as a normal fp32 number)."""
     mx = np.asarray(mx, np.float64)
     e = np.zeros(mx.shape, np.int64)
     ok = (mx > 0) & np.isfinite(mx)
     _, E = np.frexp(mx[ok])  # mx = f * 2^E, f in [0.5, 1)
     e[ok] = 15 - E
-    return np.minimum(e, 126)
+    return np.minimum(e, 116)
 
 
 def limbs(x):
