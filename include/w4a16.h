@@ -169,12 +169,16 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
  * waves, with the arithmetic of w4a16_gemm_split (limbs prescaled per row);
  * for M <= 64 otherwise the kernel of W4A16_GEMV_SKINNY reading the repacked
  * blocks whole (limbs prescaled per row and pair of groups, low limb x2^11);
- * above that one workgroup per 256 columns and 16 rows of X walks all of K
- * in slices of up to 32 groups and adds the slices in order (limbs prescaled
- * per row and K slice).  All on the fp16 matrix instructions with exact
- * weight codes and fp32 accumulation (a row of X holding Inf or NaN gives NaN
- * in that row of Y), within the tolerance of w4a16_gemm, and deterministic.  X (16-byte aligned), packed (16-byte aligned) and
- * Y (4-byte aligned) are DEVICE memory; Y must not overlap X or packed.
+ * above 64 rows, when the shape has at least 96 tiles of 128 x 128, the
+ * matrix-core tile of W4A16_PATH_TILE_MX on the repacked chunks (bit for bit
+ * its result on the public layout); otherwise one workgroup per 256 columns
+ * and 16 rows of X walks all of K in slices of up to 32 groups and adds the
+ * slices in order (limbs prescaled per row and K slice).  All on the fp16
+ * matrix instructions with exact weight codes and fp32 accumulation (a row of
+ * X holding Inf or NaN gives non-finite values in that row of Y), within the
+ * tolerance of w4a16_gemm, and deterministic.  X (16-byte aligned), packed
+ * (16-byte aligned) and Y (4-byte aligned) are DEVICE memory; Y must not
+ * overlap X or packed.
  * M == 0 or N == 0 is a no-op; otherwise errors as w4a16_gemm. */
 int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M, int64_t N,
                         int64_t K, int32_t group, void *stream);

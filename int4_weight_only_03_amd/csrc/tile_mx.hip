@@ -35,6 +35,14 @@
 // Every copy and load of an iteration is waited for before the next one's
 // barrier, one iteration after it was issued.  Images are separate __shared__
 // objects.
+//
+// Repacked weights (kPacked: the layout w4a16_repack writes, 16-row tiles by
+// 4-group steps, each 16-byte chunk one word of the step's 4 groups of one
+// row): thread t takes chunk t % 64 of tile t / 64 of the workgroup's 8, so
+// one 16-byte load per thread brings two pairs' words (every other
+// iteration), and the scales of a pair come from the step's 256-byte block.
+// The layout pads rows to 16 and groups to 4 with code 0 and scale 0, so no
+// weight or scale read needs a clamp.
 
 #include "w4a16_internal.h"
 #include "limbs.h"
@@ -77,9 +85,13 @@ __device__ __forceinline__ void lx_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// kPacked: qw points at the repacked chunks and sc at the repacked scales;
+// S4 = 4-group steps per tile, T16 = 16-row tiles.
+template <bool kPacked>
 __global__ void __launch_bounds__(64 * kLxWaves)
 tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
-        const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G, int tiles_n) {
+        const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G, int tiles_n,
+        int S4, int T16) {
   // A pair's activations: row r at 256 r.  Raw: logical chunk L (k = 4L..4L+3
   // of the pair) at physical chunk L ^ (r % 16).  Limbs: logical chunk
   // 8 limb + 4 q + b (limb 0 = hi, 1 = lo; group q; k = 8b .. 8b+7 of the
@@ -129,17 +141,38 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   }
   const char *xtile = reinterpret_cast<const char *>(X) + long(m0) * K * 4;
   // Scale copy (waves 0-3): lane i of wave w writes 4 B at 256 w + 4 i: row
-  // 32 w + i/2, group i % 2 of the pair.  Rows past N read row N-1.
+  // 32 w + i/2, group i % 2 of the pair.  Rows past N read row N-1 (public
+  // layout) or the padded rows of the last tile (repacked).
   const int srow_c = 32 * (wave & 3) + lane / 2;
-  const char *ssrc0 = reinterpret_cast<const char *>(sc) + long(std::min(n0 + srow_c, N - 1)) * G * 4;
-  // Weight words: thread t loads 8 B of W row t / 4: words 2 (t % 4) and
-  // 2 (t % 4) + 1 of the pair (group (t % 4) / 2, words R = 2 (t % 2), +1).
+  const char *ssrc0;
+  if constexpr (kPacked) {
+    // the step's block of tile n / 16: float (b * 16 + n % 16) * 4 + q
+    const int tl = std::min((n0 + srow_c) >> 4, T16 - 1);
+    ssrc0 = reinterpret_cast<const char *>(sc) + (long(tl) * S4 * 64 + ((n0 + srow_c) & 15) * 4) * 4;
+  } else {
+    ssrc0 = reinterpret_cast<const char *>(sc) + long(std::min(n0 + srow_c, N - 1)) * G * 4;
+  }
+  // Weight words.  Public layout: thread t loads 8 B of W row t / 4: words
+  // 2 (t % 4) and 2 (t % 4) + 1 of the pair (group (t % 4) / 2, words
+  // R = 2 (t % 2), +1).  Repacked: thread t loads the 16-byte chunk
+  // c + 16 R = t % 64 of tile t / 64: word R of the step's 4 groups of row
+  // 16 (t / 64) + c, i.e. word R of both groups of two pairs.
   const int tid = int(threadIdx.x);
-  const int cn = tid >> 2, ch = tid & 3, cq = ch >> 1;
-  const char *wsrc0 = reinterpret_cast<const char *>(qw) + long(std::min(n0 + cn, N - 1)) * G * 16 + 8 * ch;
+  const int cn = kPacked ? 16 * (tid >> 6) + (tid & 15) : tid >> 2;
+  const int ch = tid & 3, cq = ch >> 1;
+  const char *wsrc0;
   uint32_t cwrite[2];
+  if constexpr (kPacked) {
+    const int tl = std::min((n0 >> 4) + (tid >> 6), T16 - 1);
+    wsrc0 = reinterpret_cast<const char *>(qw) + (long(tl) * S4 * 64 + (tid & 63)) * 16;
+    const int Rw = (tid >> 4) & 3;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) cwrite[i] = uint32_t(cn * 128 + 16 * ((2 * ch + i) ^ ((cn >> 1) & 7)));
+    for (int i = 0; i < 2; ++i) cwrite[i] = uint32_t(cn * 128 + 16 * ((4 * i + Rw) ^ ((cn >> 1) & 7)));
+  } else {
+    wsrc0 = reinterpret_cast<const char *>(qw) + long(std::min(n0 + cn, N - 1)) * G * 16 + 8 * ch;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) cwrite[i] = uint32_t(cn * 128 + 16 * ((2 * ch + i) ^ ((cn >> 1) & 7)));
+  }
 
   // pair p's raw activations and scales (an odd G's last pair: its second
   // group's chunks re-read the first group; their products meet a zero scale)
@@ -152,13 +185,22 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
       lx_copy16(base + o, img + 1024 * (4 * wave + jj));
     }
     if (wave < 4) {
-      const int g = std::min(2 * p + (lane & 1), G - 1);
-      lx_copy4(ssrc0 + long(g) * 4, simg + 256 * wave);
+      if constexpr (kPacked) {
+        // step p / 2 of the tile's blocks, groups 2 (p % 2) + (lane % 2)
+        lx_copy4(ssrc0 + (long(p >> 1) * 64 + 2 * (p & 1) + (lane & 1)) * 4, simg + 256 * wave);
+      } else {
+        const int g = std::min(2 * p + (lane & 1), G - 1);
+        lx_copy4(ssrc0 + long(g) * 4, simg + 256 * wave);
+      }
     }
   };
   auto load_w = [&](int p) -> uint2 {
     const long off = long(p) * 32 - ((2 * p + 1 >= G && cq) ? 16 : 0);
     return *reinterpret_cast<const uint2 *>(wsrc0 + off);
+  };
+  // repacked: the words of pairs 2 s' and 2 s' + 1 (step s')
+  auto load_chunk = [&](int sp) -> uint4 {
+    return *reinterpret_cast<const uint4 *>(wsrc0 + long(sp) * 1024);
   };
   auto convert_w = [&](uint2 w, unsigned char *cimg) {
     const half8_t b0 = nibbles_to_f16(w.x), b1 = nibbles_to_f16(w.y);
@@ -307,11 +349,20 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   // prologue: pairs 0 and 1 copied and their weight words loaded; pair 0's
   // codes converted and its activations split
   copy_pair(lx_a0, lx_s0, 0);
-  uint2 wnext = load_w(0);
-  uint2 wlater = wnext;
-  if (P > 1) {
-    copy_pair(lx_a1, lx_s1, 1);
-    wlater = load_w(1);
+  uint2 wnext, wlater;
+  uint2 whalf = {0u, 0u};  // repacked: pair p + 3's words, loaded with pair p + 2's
+  if constexpr (kPacked) {
+    const uint4 c0 = load_chunk(0);
+    wnext = make_uint2(c0.x, c0.y);
+    wlater = make_uint2(c0.z, c0.w);
+    if (P > 1) copy_pair(lx_a1, lx_s1, 1);
+  } else {
+    wnext = load_w(0);
+    wlater = wnext;
+    if (P > 1) {
+      copy_pair(lx_a1, lx_s1, 1);
+      wlater = load_w(1);
+    }
   }
   lx_wait_vm0();
   {
@@ -349,7 +400,17 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         const uint2 wcur = wnext;  // pair p + 1's weight words
         if (p + 2 < P) {
           copy_pair(afree, sfree, p + 2);
-          wnext = load_w(p + 2);
+          if constexpr (kPacked) {
+            if ((v & 1) == 0) {  // p even: pairs p + 2 and p + 3 in one chunk
+              const uint4 c = load_chunk((p + 2) >> 1);
+              wnext = make_uint2(c.x, c.y);
+              whalf = make_uint2(c.z, c.w);
+            } else {
+              wnext = whalf;
+            }
+          } else {
+            wnext = load_w(p + 2);
+          }
         }
         Ops o;
         products_read(acur, ccur, scur, fcur, o);
@@ -387,8 +448,22 @@ hipError_t launch_tile_mx(const float *X, const int32_t *qweight, const float *s
   if (tiles < 1 || tiles > 0x7fffffffL) return hipErrorInvalidValue;
   const int G = K / kGroup;
   const int tiles_n = (N + 127) / 128;
-  hipLaunchKernelGGL(tile_mx, dim3(unsigned(tiles)), dim3(64 * kLxWaves), 0, stream, X,
-                     reinterpret_cast<const uint32_t *>(qweight), scales, Y, M, N, G, tiles_n);
+  hipLaunchKernelGGL(tile_mx<false>, dim3(unsigned(tiles)), dim3(64 * kLxWaves), 0, stream, X,
+                     reinterpret_cast<const uint32_t *>(qweight), scales, Y, M, N, G, tiles_n, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_mx_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
+                                 hipStream_t stream) {
+  const long tiles = tile_mx_tiles(M, N);
+  if (tiles < 1 || tiles > 0x7fffffffL) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  const int tiles_n = (N + 127) / 128;
+  const int T16 = (N + 15) / 16, S4 = (G + 3) / 4;
+  const unsigned char *pk = static_cast<const unsigned char *>(packed);
+  const float *psc = reinterpret_cast<const float *>(pk + size_t(T16) * S4 * 1024);
+  hipLaunchKernelGGL(tile_mx<true>, dim3(unsigned(tiles)), dim3(64 * kLxWaves), 0, stream, X,
+                     reinterpret_cast<const uint32_t *>(pk), psc, Y, M, N, G, tiles_n, S4, T16);
   return hipGetLastError();
 }
 

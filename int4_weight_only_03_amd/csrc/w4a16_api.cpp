@@ -259,6 +259,8 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
     e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
   else if (w4a16::skinny_supported(int(M)))
     e = w4a16::launch_skinny_repacked(X, packed, Y, int(M), int(N), int(K), s);
+  else if (w4a16::tile_mx_tiles(int(M), int(N)) >= w4a16::kTileMxMinTiles)
+    e = w4a16::launch_tile_mx_packed(X, packed, Y, int(M), int(N), int(K), s);
   else
     e = w4a16::launch_small_packed_loop(X, packed, Y, int(M), int(N), int(K), s);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;

@@ -57,6 +57,9 @@ long tile_mx_tiles(int M, int N);
 constexpr long kTileMxMinTiles = 96;
 hipError_t launch_tile_mx(const float *X, const int32_t *qweight, const float *scales, float *Y,
                           int M, int N, int K, hipStream_t stream);
+// the same kernel on the layout w4a16_repack writes (one expert of the grouped layout)
+hipError_t launch_tile_mx_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
+                                 hipStream_t stream);
 
 // Split-precision path: fp16 MFMA on exact weight codes and two fp16 limbs of
 // each activation; needs a caller workspace of split_workspace_bytes(M, N, K).

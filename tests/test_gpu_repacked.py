@@ -1,8 +1,9 @@
 """GPU parity of the repack entry points against the oracle, through the C ABI:
 w4a16_repack must write the oracle's pack_grouped layout (one expert) byte for
 byte, and w4a16_gemm_repacked (decode GEMV for M <= 4 when its LDS holds the
-activation limbs, otherwise the looped small-M kernel) must meet the tolerance
-on every output."""
+activation limbs, the skinny kernel up to 64 rows, the 128 x 128 matrix-core
+tile above when the shape has at least 96 such tiles, the looped small-M
+kernel otherwise) must meet the tolerance on every output."""
 
 import sys
 
@@ -122,3 +123,54 @@ def test_repacked_nonfinite_row(dev):
     assert np.all(np.isnan(Y[1])) and np.all(np.isnan(Y[4]))
     keep = [0, 2, 3, 5]
     assert oracle.compare(Y[keep], X[keep], qw, sc)["ok"]
+
+
+# the 128 x 128 matrix-core tile on repacked weights (M > 64, at least 96 tiles):
+# ragged M and N (rows padded to 16 in the layout, trailing tiles clamped), odd
+# group counts (steps padded to 4 groups), and the workload sizes' K
+TILE_SHAPES = [(1300, 1200, 160), (1200, 1290, 2080), (1025, 1536, 7168), (1100, 1300, 32),
+               (1664, 1032, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_repacked_tile_shapes(dev, M, N, K):
+    say(f"repacked tile M={M} N={N} K={K}")
+    assert -(-M // 128) * -(-N // 128) >= 96
+    X, W = workloads.random_case(M, N, K, seed=M + 7 * N + K)
+    qw, sc = oracle.quantize(W)
+    v = oracle.compare(run(X, qw, sc, dev), X, qw, sc)
+    say(f"  max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
+def test_repacked_tile_integer_exact(dev):
+    M, N, K = 1100, 1300, 288
+    rng = np.random.default_rng(31)
+    X = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+
+
+def test_repacked_tile_guard_band_and_nonfinite(dev):
+    M, N, K = 1100, 1300, 224
+    X, W = workloads.random_case(M, N, K, seed=14)
+    X[3, 17] = np.inf
+    X[1099, 200] = np.nan
+    qw, sc = oracle.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
+    Y = buf[pad:pad + M * N].view(torch.float32).view(M, N)
+    a = run(X, qw, sc, dev, Y)
+    host = buf.cpu().numpy().view(np.uint32)
+    assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
+    assert not np.any(np.isfinite(a[3])) and not np.any(np.isfinite(a[1099]))
+    keep = [m for m in range(M) if m not in (3, 1099)]
+    assert oracle.compare(a[keep], X[keep], qw, sc)["ok"]
+    # the same bits as the public layout's matrix-core tile
+    pub = binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev),
+                                  path=binding.W4A16_PATH_TILE_MX)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[keep].view(np.uint32), pub.cpu().numpy()[keep].view(np.uint32))
