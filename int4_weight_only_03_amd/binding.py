@@ -104,10 +104,18 @@ def header_functions() -> list[str]:
 
 
 def load(path: str | None = None):
-    """Load the library (building it first only if no build exists)."""
+    """Load the library (building it first only if no build exists).
+
+    torch is imported first: its wheel carries its own HIP runtime
+    (libamdhip64.so.7, with its own ROCr), and the library's dependency on
+    libamdhip64.so.7 then binds to that already-loaded copy.  Loaded before
+    torch, the library would bring in the system copy, torch would add its
+    own, and whichever runtime initialised the GPU second would see no device
+    (launches fail with hipErrorNoDevice)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
+    import torch  # noqa: F401  (see above: one HIP runtime per process)
     p = path or LIB_PATH
     if not os.path.exists(p):
         from . import build as _build

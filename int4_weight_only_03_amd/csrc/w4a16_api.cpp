@@ -45,6 +45,13 @@ int validate_gemm(const float *X, const int32_t *qweight, const float *scales, f
   return W4A16_OK;
 }
 
+// Every launch helper reports hipGetLastError() after its launches.  That
+// per-thread slot also holds the status of the caller's own earlier HIP calls
+// (a non-sticky error left there by someone else's call would otherwise be
+// reported as this call's failure), so it is cleared right before a launch.
+// Sticky errors (a fault of earlier work) cannot be cleared and still surface.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 int select_path(int64_t M, int64_t N, int64_t K) {
   (void)K;
   if (M <= w4a16::kGemvMaxM) return W4A16_PATH_GEMV;
@@ -83,6 +90,8 @@ int w4a16_gemm_path(const float *X, const int32_t *qweight, const float *scales,
   if (st != W4A16_OK || M == 0 || N == 0) return st;
   if (path == W4A16_PATH_AUTO) path = select_path(M, N, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_stale_hip_error();
+
   hipError_t e;
   switch (path) {
     case W4A16_PATH_GEMV:
@@ -112,6 +121,8 @@ int w4a16_read_floor(const void *const *ptrs, const int64_t *bytes, int32_t n, i
     if (!aligned(ptrs[i], 16) || bytes[i] % 16 != 0) return W4A16_ERR_ALIGN;
     b[i] = long(bytes[i]);
   }
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_read_floor(ptrs, b, n, threads, loads,
                                           static_cast<unsigned *>(sink),
                                           reinterpret_cast<hipStream_t>(stream));
@@ -128,6 +139,8 @@ int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scale
   if (F < 0 || F > W4A16_MAX_N / 2) return F < 0 ? W4A16_ERR_ARG : W4A16_ERR_SHAPE;
   int st = validate_gemm(X, qweight, scales, Y, M, 2 * F, K, group, F);
   if (st != W4A16_OK || M == 0 || F == 0) return st;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_gemv_swiglu(X, qweight, scales, Y, int(M), int(F), int(K),
                                            reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -154,6 +167,8 @@ int w4a16_gemm_grouped(const float *X, const int32_t *token_index, const int32_t
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, qweight, bq) || overlaps(Y, by, scales, bs) ||
       overlaps(Y, by, token_index, bi) || overlaps(Y, by, expert_offsets, bo))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_grouped(X, token_index, expert_offsets, qweight, scales, Y,
                                        int(T), int(R), int(E), int(N), int(K),
                                        reinterpret_cast<hipStream_t>(stream));
@@ -182,6 +197,8 @@ int w4a16_grouped_pack(const int32_t *qweight, const float *scales, int64_t E, i
   const size_t bs = size_t(E) * size_t(N) * size_t(K / W4A16_GROUP) * 4;
   if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_grouped_pack(qweight, scales, packed, int(E), int(N), int(K),
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -210,6 +227,8 @@ int w4a16_gemm_grouped_packed(const float *X, const int32_t *token_index,
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp) || overlaps(Y, by, token_index, bi) ||
       overlaps(Y, by, expert_offsets, bo))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_grouped_packed(X, token_index, expert_offsets, packed, Y, int(T),
                                               int(R), int(E), int(N), int(K),
                                               reinterpret_cast<hipStream_t>(stream));
@@ -236,6 +255,8 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
   const size_t bq = size_t(N) * size_t(K) / 2, bs = size_t(N) * size_t(K / W4A16_GROUP) * 4;
   if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_grouped_pack(qweight, scales, packed, 1, int(N), int(K),
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -254,6 +275,8 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
   const size_t bp = w4a16::grouped_pack_bytes(1, int(N), int(K));
   if (overlaps(Y, by, X, bx) || overlaps(Y, by, packed, bp)) return W4A16_ERR_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_stale_hip_error();
+
   hipError_t e;
   if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
     e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
@@ -292,6 +315,8 @@ int w4a16_gemm_small_packed(const float *X, const void *packed, float *Y, int64_
         overlaps(workspace, need, Y, by))
       return W4A16_ERR_ARG;
   }
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_small_packed(X, packed, Y, int(M), int(N), int(K), workspace,
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -314,6 +339,8 @@ int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y
   if (need > W4A16_NOALLOC_SCRATCH_BYTES) return W4A16_ERR_SCRATCH;
   void *ws = nullptr;
   if (need > 0 && w4a16::noalloc_scratch(&ws) != hipSuccess) return W4A16_ERR_HIP;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_small_packed(X, packed, Y, int(M), int(N), int(K), ws,
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -350,6 +377,8 @@ int w4a16_gemm_split(const float *X, const int32_t *qweight, const float *scales
   if (overlaps(workspace, need, X, bx) || overlaps(workspace, need, qweight, bq) ||
       overlaps(workspace, need, scales, bs) || overlaps(workspace, need, Y, by))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_split(X, qweight, scales, Y, int(M), int(N), int(K), workspace,
                                      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -375,6 +404,8 @@ int w4a16_split_pack(const int32_t *qweight, const float *scales, int64_t N, int
   const size_t bq = size_t(N) * size_t(K) / 2, bs = size_t(N) * size_t(K / W4A16_GROUP) * 4;
   if (overlaps(packed, need, qweight, bq) || overlaps(packed, need, scales, bs))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_split_pack(qweight, scales, packed, int(N), int(K),
                                           reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
@@ -398,6 +429,8 @@ int w4a16_gemm_split_packed(const float *X, const void *packed, float *Y, int64_
   if (overlaps(workspace, need, X, bx) || overlaps(workspace, need, packed, bp) ||
       overlaps(workspace, need, Y, by))
     return W4A16_ERR_ARG;
+  clear_stale_hip_error();
+
   hipError_t e = w4a16::launch_split_packed(X, packed, Y, int(M), int(N), int(K), workspace,
                                             reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;

@@ -248,3 +248,21 @@ def test_native_library_is_loaded(dev):
     path = os.path.realpath(binding.LIB_PATH)
     maps = open("/proc/self/maps").read()
     assert path in maps
+
+
+def test_stale_caller_error_not_reported(dev):
+    # an error left in HIP's per-thread slot by the caller's own earlier call
+    # (here: an invalid device ordinal, rejected on the host) is not this
+    # library's failure: the next GEMM still succeeds and is correct
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    X, W = workloads.random_case(3, 200, 256, seed=21)
+    qw, sc = oracle.quantize(W)
+    for path in (binding.W4A16_PATH_GEMV, binding.W4A16_PATH_TILE_MX):
+        assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+        Y = binding.w4a16_gemm_path(torch.from_numpy(X).to(dev), torch.from_numpy(qw).to(dev),
+                                    torch.from_numpy(sc).to(dev), path=path)
+        torch.cuda.synchronize()
+        check(Y.cpu().numpy(), X, qw, sc, f"after a stale caller error, path {path}")
+    assert hip.hipGetLastError() == 0
