@@ -7,6 +7,8 @@
 """
 
 import ctypes
+import os
+import sys
 
 import numpy as np
 import pytest
@@ -430,3 +432,23 @@ def test_small_packed_noalloc_errors(lib):
     assert g(X_, P_, P_ + 64) == ARG                      # Y overlaps packed
     assert g(None, None, None, m=0) == OK
     assert g(None, None, None, n=0) == OK
+
+
+def test_one_hip_runtime_per_process():
+    # loading the library first in a fresh process still maps a single HIP
+    # runtime, torch's: a second copy would initialise the GPU a second time
+    # and see no device
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from int4_weight_only_03_amd import binding\n"
+            "binding.load()\n"
+            "import torch, os\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(sorted(maps)); print(os.path.dirname(torch.__file__))\n") % root
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    maps_line, torch_dir = out.stdout.strip().splitlines()[-2:]
+    maps = eval(maps_line)
+    assert len(maps) == 1, maps
+    assert os.path.realpath(maps[0]).startswith(os.path.realpath(torch_dir)), (maps, torch_dir)
