@@ -30,7 +30,10 @@
  * anything is launched, and reported as a status code (Y untouched).  Work is
  * enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  * A launch that the HIP runtime refuses returns W4A16_ERR_HIP; faults that
- * happen later surface at the caller's next synchronisation.
+ * happen later surface at the caller's next synchronisation.  Before it
+ * launches, an entry point clears HIP's per-thread error slot, so that an
+ * error left there by the caller's own earlier HIP calls is not reported as
+ * this call's (sticky errors of earlier faults cannot be cleared and do).
  */
 #ifndef W4A16_H
 #define W4A16_H
