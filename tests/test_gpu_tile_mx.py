@@ -162,3 +162,22 @@ def test_same_as_fp32_tile_within_tolerance(dev):
     qw, sc = oracle.quantize(W)
     check(run(X, qw, sc, dev), X, qw, sc, "tile-mx 384x512x2048")
     check(run(X, qw, sc, dev, path=binding.W4A16_PATH_TILE), X, qw, sc, "tile 384x512x2048")
+
+
+@pytest.mark.parametrize("N,want", [(12161, binding.W4A16_PATH_TILE_MX), (12160, binding.W4A16_PATH_TILE)])
+def test_dispatch_boundary_every_output(dev, N, want):
+    # 65 rows: the smallest M above the GEMV path, one 128-row tile with 63
+    # padded rows; 96 tiles of 128 x 128 take the matrix-core tile (N ragged),
+    # 95 the fp32 tile; w4a16_gemm and, for the matrix-core tile, the repacked
+    # entry point on the same weights
+    M, K = 65, 96
+    assert binding.w4a16_select_path(M, N, K) == want
+    X, W = workloads.random_case(M, N, K, seed=N)
+    qw, sc = oracle.quantize(W)
+    Y = run(X, qw, sc, dev, path=binding.W4A16_PATH_AUTO)
+    check(Y, X, qw, sc, f"w4a16_gemm M={M} N={N}")
+    if want == binding.W4A16_PATH_TILE_MX:
+        packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
+        Yr = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, N)
+        torch.cuda.synchronize()
+        assert np.array_equal(Yr.cpu().numpy().view(np.uint32), Y.view(np.uint32))
