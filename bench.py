@@ -19,8 +19,9 @@ streaming-read floor of the same bytes (a plain read of X, qweight and scales
 over the same rotating buffers, `w4a16_read_floor`, best of six launch
 shapes), the fp32-FMA GEMV beside the matrix-core GEMV for the M=1 decodes,
 the fp32 tiled path beside the matrix-core tile for the prefill, and the other
-entry points for the two larger shapes (repacked, small-packed, split on
-packed weights; their one-time repack is timed apart).
+entry points (repacked weights for the decodes; repacked, small-packed and
+split on packed weights for the two larger shapes; their one-time repack is
+timed apart).
 
 With --workload, one JSON line per (workload, path) instead (for profiling):
 paths auto, gemv, gemv-fma, tile, tile-mx, split, packed, swiglu, repacked,
@@ -82,8 +83,8 @@ PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
-                "repacked": ["packed_gemv.hip", "skinny.hip", "small_packed.hip", "gemv_common.h",
-                             "limbs.h"],
+                "repacked": ["gemv_mfma.hip", "packed_gemv.hip", "skinny.hip", "tile_mx.hip",
+                             "small_packed.hip", "gemv_common.h", "limbs.h"],
                 "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"],
                 "read-floor": ["read_floor.hip", "gemv_common.h"]}
 # launch shapes of the streaming-read floor: (threads per block, 16-byte loads per thread)
@@ -462,10 +463,11 @@ def headline(args) -> None:
             f.pop("_y0")
             r["fp32_fma_gemv"] = {k: f[k] for k in ("us_per_step", "GB_s", "hbm_frac", "dtype",
                                                    "per_launch_event_us_median")}
-        if name in ("verify_tree", "prefill"):
+        others = {"decode_gate_up": ("repacked",), "decode_down": ("repacked",),
+                  "verify_tree": ("small-packed", "repacked", "packed"),
+                  "prefill": ("tile", "packed", "repacked")}.get(name, ())
+        if others:
             alts = {}
-            others = (("small-packed", "repacked", "packed") if wl.M <= 64
-                      else ("tile", "packed", "repacked"))
             for p in others:
                 a = prob.measure(p, steps, args.warmup)
                 a.pop("_y0")

@@ -167,10 +167,13 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
                  int64_t K, int32_t group, void *stream);
 
 /* Y[M][N] = X[M][K] . dequant(W)^T with W repacked by w4a16_repack(..., N, K,
- * ...).  No workspace and no allocation: for M <= 4 (when the activation limbs
- * fit the kernel's LDS) a decode GEMV whose workgroups split K over their
- * waves, with the arithmetic of w4a16_gemm_split (limbs prescaled per row);
- * for M <= 64 otherwise the kernel of W4A16_GEMV_SKINNY reading the repacked
+ * ...).  No workspace and no allocation: for M <= 8 and K <= 8192 the decode
+ * GEMV of W4A16_GEMV_MFMA, each lane gathering its group's 16 bytes from four
+ * repacked chunks (bit for bit the result of w4a16_gemm on the public
+ * layout); for M <= 4 with longer K (when the activation limbs fit the
+ * kernel's LDS) a decode GEMV whose workgroups split K over their waves, with
+ * the arithmetic of w4a16_gemm_split (limbs prescaled per row); for M <= 64
+ * otherwise the kernel of W4A16_GEMV_SKINNY reading the repacked
  * blocks whole (limbs prescaled per row and pair of groups, low limb x2^11);
  * above 64 rows, when the shape has at least 96 tiles of 128 x 128, the
  * matrix-core tile of W4A16_PATH_TILE_MX on the repacked chunks (bit for bit

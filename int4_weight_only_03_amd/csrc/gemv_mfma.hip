@@ -76,10 +76,18 @@ static_assert(mx_wave_lds(8) >= 8 * 4 * 4 * sizeof(float), "partials fit the lim
 // qw/sc (kSw: gate rows there, up rows N further) against MT activation rows
 // xr[m] (rows past the real ones point at a real row and feed only results
 // that are not stored), results to yr[m][n] for yr[m] != nullptr and n < N.
-template <int MT, int R, bool kSw>
+//
+// kPk: W in the repacked layout of w4a16_repack instead (qw its weight
+// blocks, sc its scales, S4 steps of 4 groups per 16-row tile, T16 tiles):
+// each lane gathers the same 16 bytes (words 0..3 of its group and row) from
+// four chunks 256 bytes apart, so the arithmetic and its result are those of
+// the public layout, bit for bit.
+template <int MT, int R, bool kSw, bool kPk>
 __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint4 *__restrict__ qw,
                                         const float *__restrict__ sc, float *const (&yr)[MT],
-                                        int N, int G, long rowbase, unsigned char *smem) {
+                                        int N, int G, long rowbase, unsigned char *smem, int S4,
+                                        long T16) {
+  static_assert(!(kSw && kPk), "the fused SwiGLU reads the public layout only");
   constexpr int RL = kSw ? 2 * R : R;  // row quads per lane (gate quads, then up quads)
   constexpr int MS = (MT + 1) / 2;     // A operands of 4 limb rows (2 activation rows each)
   const int lane = threadIdx.x & 63;
@@ -104,7 +112,32 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
   }
   uint4 w[RL];
   float s[RL];
-  {
+  if constexpr (kPk) {
+    // the workgroup's rows lie in tiles t0 .. t0 + 1 (4R <= 32 rows, rowbase a
+    // multiple of 4R); the buffers end at the last tile, so rows past it read
+    // zero, and the tiles' padding rows and groups hold weight 0, scale 0
+    const long t0 = rowbase >> 4;
+    const long t1 = std::min((rowbase + 4 * R + 15) >> 4, T16);
+    const int bytes = int(t1 - t0) * S4 * 1024;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4 *>(qw + t0 * S4 * 64), (short)0, bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(sc + t0 * S4 * 64), (short)0, bytes / 4, kRsrcWord3);
+    const bool in = g < 4 * S4;  // past the padded groups: offsets past the buffers
+    const int st = g >> 2, gq = g & 3;
+#pragma unroll
+    for (int q = 0; q < RL; ++q) {
+      const int rl = int(rowbase & 15) + 4 * q + j;  // row within tile t0 (and t0 + 1)
+      const int blk = (rl >> 4) * S4 + st;
+      const uint32_t ow = in ? uint32_t(((blk * 64 + (rl & 15)) * 16) + gq * 4) : 0x40000000u;
+      const uint32_t os = in ? uint32_t(((blk * 16 + (rl & 15)) * 4 + gq) * 4) : 0x40000000u;
+      w[q].x = __builtin_amdgcn_raw_buffer_load_b32(rw, ow, 0, 2);
+      w[q].y = __builtin_amdgcn_raw_buffer_load_b32(rw, ow + 256, 0, 2);
+      w[q].z = __builtin_amdgcn_raw_buffer_load_b32(rw, ow + 512, 0, 2);
+      w[q].w = __builtin_amdgcn_raw_buffer_load_b32(rw, ow + 768, 0, 2);
+      s[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 2));
+    }
+  } else {
     const int rows = int(std::min(long(N) - rowbase, long(4 * R)));
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint4 *>(qw + rowbase * G), (short)0, rows * G * 16, kRsrcWord3);
@@ -234,10 +267,10 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
 
 // N: outputs per row of Y (F for kSw, whose W has 2N rows).  MT = 4 serves
 // M = 3 and 4, MT = 8 serves M = 5 .. 8.
-template <int MT, int R, bool kSw>
+template <int MT, int R, bool kSw, bool kPk>
 __global__ void __launch_bounds__(1024)
 gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
-        float *__restrict__ Y, int M, int N, int G) {
+        float *__restrict__ Y, int M, int N, int G, int S4, long T16) {
   extern __shared__ __align__(16) unsigned char smem[];
   const long K = long(G) * kGroup;
   const float *xr[MT];
@@ -247,22 +280,24 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
     xr[m] = X + (m < M ? m : 0) * K;
     yr[m] = m < M ? Y + long(m) * N : nullptr;
   }
-  mx_pass<MT, R, kSw>(xr, qw, sc, yr, N, G, long(blockIdx.x) * (4 * R), smem);
+  mx_pass<MT, R, kSw, kPk>(xr, qw, sc, yr, N, G, long(blockIdx.x) * (4 * R), smem, S4, T16);
 }
 
-template <int MT, int R, bool kSw>
-hipError_t run_mx(const float *X, const int32_t *qw, const float *sc, float *Y, int M, int N,
+template <int MT, int R, bool kSw, bool kPk>
+hipError_t run_mx(const float *X, const void *qw, const float *sc, float *Y, int M, int N,
                   int G, hipStream_t stream) {
   const int waves = (G + 15) / 16;
   const int blocks = int((long(N) + 4 * R - 1) / (4 * R));
-  hipLaunchKernelGGL((gemv_mx<MT, R, kSw>), dim3(blocks), dim3(waves * 64),
+  const int S4 = (G + 3) / 4;
+  const long T16 = (long(N) + 15) / 16;
+  hipLaunchKernelGGL((gemv_mx<MT, R, kSw, kPk>), dim3(blocks), dim3(waves * 64),
                      waves * mx_wave_lds(MT), stream, X, reinterpret_cast<const uint4 *>(qw), sc,
-                     Y, M, N, G);
+                     Y, M, N, G, S4, T16);
   return hipGetLastError();
 }
 
-template <int MT, bool kSw>
-hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc, float *Y, int M,
+template <int MT, bool kSw, bool kPk = false>
+hipError_t dispatch_mx(int R, const float *X, const void *qw, const float *sc, float *Y, int M,
                        int N, int G, hipStream_t stream) {
   // row quads per lane are capped so that no variant spills: 8 only for the
   // plain GEMV of up to 2 rows, 2 (1 with kSw) for 8 rows
@@ -270,15 +305,15 @@ hipError_t dispatch_mx(int R, const float *X, const int32_t *qw, const float *sc
   R = std::min(R, kCap);
   switch (R) {
     case 8:
-      if constexpr (kCap >= 8) return run_mx<MT, 8, kSw>(X, qw, sc, Y, M, N, G, stream);
+      if constexpr (kCap >= 8) return run_mx<MT, 8, kSw, kPk>(X, qw, sc, Y, M, N, G, stream);
       else return hipErrorInvalidValue;
     case 4:
-      if constexpr (kCap >= 4) return run_mx<MT, 4, kSw>(X, qw, sc, Y, M, N, G, stream);
+      if constexpr (kCap >= 4) return run_mx<MT, 4, kSw, kPk>(X, qw, sc, Y, M, N, G, stream);
       else return hipErrorInvalidValue;
     case 2:
-      if constexpr (kCap >= 2) return run_mx<MT, 2, kSw>(X, qw, sc, Y, M, N, G, stream);
+      if constexpr (kCap >= 2) return run_mx<MT, 2, kSw, kPk>(X, qw, sc, Y, M, N, G, stream);
       else return hipErrorInvalidValue;
-    default: return run_mx<MT, 1, kSw>(X, qw, sc, Y, M, N, G, stream);
+    default: return run_mx<MT, 1, kSw, kPk>(X, qw, sc, Y, M, N, G, stream);
   }
 }
 
@@ -325,6 +360,23 @@ hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const
     case 3:
     case 4: return dispatch_mx<4, true>(R, X, qweight, scales, Y, M, F, G, stream);
     default: return dispatch_mx<8, true>(R, X, qweight, scales, Y, M, F, G, stream);
+  }
+}
+
+hipError_t launch_gemv_mfma_packed(const float *X, const void *packed, float *Y, int M, int N,
+                                   int K, hipStream_t stream) {
+  if (!gemv_mfma_supported(M, K)) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  const int R = gemv_mfma_quads(N);
+  // the scales follow the T16 * S4 kilobyte weight blocks
+  const float *psc = reinterpret_cast<const float *>(
+      static_cast<const unsigned char *>(packed) + ((long(N) + 15) / 16) * ((G + 3) / 4) * 1024);
+  switch (M) {
+    case 1: return dispatch_mx<1, false, true>(R, X, packed, psc, Y, M, N, G, stream);
+    case 2: return dispatch_mx<2, false, true>(R, X, packed, psc, Y, M, N, G, stream);
+    case 3:
+    case 4: return dispatch_mx<4, false, true>(R, X, packed, psc, Y, M, N, G, stream);
+    default: return dispatch_mx<8, false, true>(R, X, packed, psc, Y, M, N, G, stream);
   }
 }
 

@@ -278,7 +278,9 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
   clear_stale_hip_error();
 
   hipError_t e;
-  if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
+  if (w4a16::gemv_mfma_supported(int(M), int(K)))
+    e = w4a16::launch_gemv_mfma_packed(X, packed, Y, int(M), int(N), int(K), s);
+  else if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
     e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
   else if (w4a16::skinny_supported(int(M)))
     e = w4a16::launch_skinny_repacked(X, packed, Y, int(M), int(N), int(K), s);

@@ -30,6 +30,10 @@ hipError_t launch_gemv_mfma(const float *X, const int32_t *qweight, const float 
 // the same with the fused gate/up SwiGLU epilogue (W: 2F rows, gate then up; Y[M][F])
 hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const float *scales,
                                    float *Y, int M, int F, int K, hipStream_t stream);
+// The same kernel on the weights of w4a16_repack (bit for bit its result on
+// the public layout).
+hipError_t launch_gemv_mfma_packed(const float *X, const void *packed, float *Y, int M, int N,
+                                   int K, hipStream_t stream);
 
 // Skinny GEMM (1 <= M <= kSkinnyMaxM) on the fp16 matrix instructions: exact
 // weight codes, two fp16 limbs of each activation prescaled per row and pair

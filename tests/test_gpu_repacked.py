@@ -1,8 +1,10 @@
 """GPU parity of the repack entry points against the oracle, through the C ABI:
 w4a16_repack must write the oracle's pack_grouped layout (one expert) byte for
-byte, and w4a16_gemm_repacked (decode GEMV for M <= 4 when its LDS holds the
-activation limbs, the skinny kernel up to 64 rows, the 128 x 128 matrix-core
-tile above when the shape has at least 96 such tiles, the looped small-M
+byte, and w4a16_gemm_repacked (the matrix-core decode GEMV of w4a16_gemm for
+M <= 8 and K <= 8192, bit for bit its result on the public layout; the
+split-K decode GEMV for M <= 4 with longer K when its LDS holds the
+activation limbs; the skinny kernel up to 64 rows; the 128 x 128 matrix-core
+tile above when the shape has at least 96 such tiles; the looped small-M
 kernel otherwise) must meet the tolerance on every output."""
 
 import sys
@@ -56,12 +58,15 @@ def test_repack_matches_oracle_bytes(dev, N, K):
 
 
 SHAPES = [
-    # decode kernel (M <= 4, limbs fit its LDS)
-    (1, 512, 256), (2, 70, 224), (3, 33, 96), (4, 129, 512), (1, 16, 32), (1, 100, 38144),
-    (4, 64, 9344), (2, 300, 7168),
-    # looped small-M kernel: M > 4, or K too long for the decode kernel's LDS
-    (1, 40, 38176), (4, 20, 9376), (5, 17, 32), (8, 100, 1056), (17, 70, 160), (33, 45, 4128),
-    (63, 33, 96), (64, 300, 7168), (65, 129, 224), (130, 200, 320), (300, 260, 256),
+    # matrix-core decode GEMV (M <= 8, K <= 8192)
+    (1, 512, 256), (2, 70, 224), (3, 33, 96), (4, 129, 512), (1, 16, 32), (2, 300, 7168),
+    (5, 17, 32), (8, 100, 1056),
+    # split-K decode GEMV (M <= 4, K > 8192, limbs fit its LDS)
+    (1, 100, 38144), (4, 64, 9344),
+    # skinny kernel (K too long for the split-K decode kernel's LDS, or 9..64 rows)
+    (1, 40, 38176), (4, 20, 9376), (17, 70, 160), (33, 45, 4128), (63, 33, 96), (64, 300, 7168),
+    # looped small-M kernel above 64 rows with few tiles
+    (65, 129, 224), (130, 200, 320), (300, 260, 256),
 ]
 
 
@@ -71,6 +76,28 @@ def test_repacked_shapes(dev, M, N, K):
     X, W = workloads.random_case(M, N, K, seed=M * 17 + N + K)
     qw, sc = oracle.quantize(W)
     v = oracle.compare(run(X, qw, sc, dev), X, qw, sc)
+    say(f"  max err/bound {v['max_ratio']:.3e}")
+    assert v["ok"], v
+
+
+# (M, N, K): row counts of every A-operand form (1, 2, 4, 8 activation rows),
+# quads per lane 1..8 (N from 17 to 7168), group counts that leave 1..3
+# padding groups in the last 4-group step (G = 1, 3, 65, 66, 255) and the
+# longest K (G = 256, 16 waves)
+DECODE_BITWISE = [(1, 17, 32), (2, 33, 96), (3, 300, 2080), (4, 1000, 2112), (5, 129, 8160),
+                  (6, 70, 8192), (7, 4096, 224), (8, 900, 7168), (1, 7168, 2048), (1, 4096, 7168)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_BITWISE)
+def test_repacked_decode_matches_public_bitwise(dev, M, N, K):
+    say(f"repacked decode GEMV M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M * 29 + N + K)
+    qw, sc = oracle.quantize(W)
+    got = run(X, qw, sc, dev)
+    pub = binding.w4a16_gemm(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), pub.cpu().numpy().view(np.uint32))
+    v = oracle.compare(got, X, qw, sc)
     say(f"  max err/bound {v['max_ratio']:.3e}")
     assert v["ok"], v
 
