@@ -79,8 +79,9 @@ extern "C" {
 
 /* Kernel paths behind w4a16_gemm. */
 #define W4A16_PATH_AUTO 0     /* what w4a16_gemm uses: w4a16_select_path() */
-#define W4A16_PATH_GEMV 1     /* decode/verify path (M <= 64): dequant-on-the-fly kernels that
-                                 stream the weights once; which one: w4a16_gemv_kernel */
+#define W4A16_PATH_GEMV 1     /* decode/verify path: dequant-on-the-fly kernels (the decode
+                                 GEMVs, the skinny kernel at any M); which one:
+                                 w4a16_gemv_kernel */
 #define W4A16_PATH_TILE 2     /* tiled path: fp32 MFMA 32x32x2 on dequantized tiles */
 #define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
                                  exact (q - 8) codes and two fp16 limbs of each activation */
@@ -172,14 +173,12 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
  * repacked chunks (bit for bit the result of w4a16_gemm on the public
  * layout); for M <= 4 with longer K (when the activation limbs fit the
  * kernel's LDS) a decode GEMV whose workgroups split K over their waves, with
- * the arithmetic of w4a16_gemm_split (limbs prescaled per row); for M <= 64
- * otherwise the kernel of W4A16_GEMV_SKINNY reading the repacked
- * blocks whole (limbs prescaled per row and pair of groups, low limb x2^11);
- * above 64 rows, when the shape has at least 96 tiles of 128 x 128, the
- * matrix-core tile of W4A16_PATH_TILE_MX on the repacked chunks (bit for bit
- * its result on the public layout); otherwise one workgroup per 256 columns
- * and 16 rows of X walks all of K in slices of up to 32 groups and adds the
- * slices in order (limbs prescaled per row and K slice).  All on the fp16
+ * the arithmetic of w4a16_gemm_split (limbs prescaled per row); otherwise,
+ * where w4a16_select_path picks the GEMV path, the kernel of W4A16_GEMV_SKINNY
+ * reading the repacked blocks whole (limbs prescaled per row and pair of
+ * groups, low limb x2^11), and where it picks W4A16_PATH_TILE_MX that
+ * matrix-core tile on the repacked chunks (bit for bit its result on the
+ * public layout).  All on the fp16
  * matrix instructions with exact weight codes and fp32 accumulation (a row of
  * X holding Inf or NaN gives non-finite values in that row of Y), within the
  * tolerance of w4a16_gemm, and deterministic.  X (16-byte aligned), packed
@@ -352,9 +351,9 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
                                  group's maximum (the low limb carried x2^11); products exact
                                  in fp32, fp32 accumulation, one fp32 multiply per (row,
                                  group) applies scale * 2^-e */
-#define W4A16_GEMV_FMA 2      /* M <= 2 with K > 8192, or M > 64 forced onto the GEMV path:
-                                 one fp32 FMA per weight, activations in VGPRs */
-#define W4A16_GEMV_SKINNY 3   /* 3 <= M <= 64 otherwise (the tree-verification batches):
+#define W4A16_GEMV_FMA 2      /* M <= 2 with K > 8192: one fp32 FMA per weight, activations
+                                 in VGPRs */
+#define W4A16_GEMV_SKINNY 3   /* M >= 3 otherwise (the tree-verification batches and beyond):
                                  v_mfma_f32_16x16x32_f16 on exact weight codes and two fp16
                                  limbs of each activation, prescaled by a power of two per
                                  row and pair of groups, the low limb x2^11 and met by the
@@ -369,10 +368,15 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
  * Knowledge".) */
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
 
-/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV, _TILE_MX or _TILE):
- * the GEMV path for M <= 64; above that the matrix-core tile when the shape has at
- * least 96 tiles of 128 x 128 (ceil(M/128) * ceil(N/128) >= 96), the fp32 tiled
- * path otherwise.  Host only; no GPU use. */
+/* The path W4A16_PATH_AUTO takes for this shape (W4A16_PATH_GEMV or _TILE_MX): the
+ * GEMV path for M <= 64; above that the cheaper of the skinny kernel and the
+ * 128 x 128 matrix-core tile by rounds over 256 compute units, each weighted by
+ * its workgroup's measured cost: ceil(ceil(M/16) * ceil(N/(16 NT)) / 256) * NT
+ * for the skinny kernel (NT = 4, 2 or 1 column tiles of 16, the widest that
+ * leaves at least 256 workgroups) against ceil(ceil(M/128) * ceil(N/128) / 256)
+ * * 33 for the tile, the skinny kernel on a tie.  The fp32 tiled path
+ * (W4A16_PATH_TILE) is no longer chosen: the skinny kernel is about twice as
+ * fast on every shape where the tile does not win.  Host only; no GPU use. */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 
 /*

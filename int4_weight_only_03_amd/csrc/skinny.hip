@@ -1,5 +1,5 @@
 // Skinny W4A16 GEMM on the fp16 matrix cores: Y[M][N] = X[M][K] . dequant(W)^T
-// for a few dozen rows of X, with no workspace.
+// for a few dozen to a few hundred rows of X, with no workspace.
 //
 // The pages' speculative decoder scores a tree of draft tokens in one batch
 // against every weight ("The Quiet Commit: How a Single Documentation Edit
@@ -7,7 +7,9 @@
 // Context: A Native DDTree Engine Takes Shape"): M of a few dozen rows, too
 // many for a GEMV and too few to reuse a weight tile in fp32 matrix
 // instructions at their peak.  This kernel is w4a16_gemm's path for
-// 9 <= M <= 64 (and for 3 <= M <= 8 when K is beyond the decode GEMV's limit).
+// 9 <= M <= 64 (and for 3 <= M <= 8 when K is beyond the decode GEMV's limit),
+// and above 64 rows while its rounds of workgroups cost less than those of the
+// 128 x 128 matrix-core tile (skinny_preferred).
 //
 // Arithmetic: the decode GEMV's (exact weight codes, two fp16 limbs of each
 // prescaled activation, fp32 accumulation), with the power of two taken per
@@ -121,14 +123,14 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   // swizzle: the 16 rows an operand read touches at one logical chunk fall in
   // 16 distinct chunks of one 256-byte window, hence distinct LDS banks).
   // Rows past M read row M-1.  Every copy's address is a wave-uniform base
-  // (the step's first group) plus a fixed per-lane byte offset below 2^32 (X
-  // holds at most 64 rows of 2^17 floats).
+  // (the tile's first row, the step's first group) plus a fixed per-lane byte
+  // offset below 2^23 (16 rows of at most 2^17 floats).
   uint32_t xoff[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const int rho = 2 * j + lane / 32;
     const int L = (lane & 31) ^ (rho & 15);
-    xoff[j] = uint32_t(std::min(m0 + rho, M - 1)) * uint32_t(G) * 128u + 16u * uint32_t(L);
+    xoff[j] = uint32_t(std::min(m0 + rho, M - 1) - m0) * uint32_t(G) * 128u + 16u * uint32_t(L);
   }
   // Weight copy t: lane i writes 16 bytes at slot offset 1024 t + 16 i: W row
   // n0 + 16 t + i / 4, position i % 4 of that row's 64 bytes, which holds
@@ -187,7 +189,7 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
       }
     }
     if (!tail) {
-      const char *xb = reinterpret_cast<const char *>(X) + gs * 128;
+      const char *xb = reinterpret_cast<const char *>(X) + long(m0) * G * 128 + gs * 128;
 #pragma unroll
       for (int j = 0; j < kCopies; ++j) {
         const char *src = xb + xoff[j];
@@ -204,7 +206,7 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         }
       }
     } else {
-      const char *xb = reinterpret_cast<const char *>(X);
+      const char *xb = reinterpret_cast<const char *>(X) + long(m0) * G * 128;
 #pragma unroll
       for (int j = 0; j < kCopies; ++j) {
         const int rho = 2 * j + lane / 32;
@@ -472,15 +474,15 @@ SkPlan plan_skinny(int M, int N) {
   p.tiles_m = (M + 16 * p.MT - 1) / (16 * p.MT);
 #else
   p.MT = 1;
-  p.tiles_m = (M + 15) / 16;
+  p.tiles_m = int((long(M) + 15) / 16);
   p.NT = 1;
   for (int nt = 4; nt > 1; nt /= 2)
-    if (long((N + 16 * nt - 1) / (16 * nt)) * p.tiles_m >= 256) {
+    if ((long(N) + 16 * nt - 1) / (16 * nt) * p.tiles_m >= 256) {
       p.NT = nt;
       break;
     }
 #endif
-  p.tiles_n = (N + 16 * p.NT - 1) / (16 * p.NT);
+  p.tiles_n = int((long(N) + 16 * p.NT - 1) / (16 * p.NT));
   return p;
 }
 
@@ -513,7 +515,21 @@ hipError_t dispatch_skinny(const float *X, const void *qw, const float *sc, floa
 
 }  // namespace
 
-bool skinny_supported(int M) { return M >= 1 && M <= kSkinnyMaxM; }
+bool skinny_supported(int M) { return M >= 1; }
+
+// Rounds of workgroups over the 256 compute units, weighted by the work of
+// one: a skinny workgroup of 16 x 16 NT outputs costs NT units, a 128 x 128
+// matrix-core tile 33 (per round, both in proportion to K: 24.2 us for a round
+// of 16 x 64 skinny tiles and 200 us for a round of 128 x 128 tiles at
+// K = 7168, measured on MI355X).  Below the crossover the tile's rounds are
+// mostly idle compute units (one workgroup per unit for all of K).
+bool skinny_preferred(int M, int N) {
+  if (M <= kSkinnyAlwaysM) return true;
+  const SkPlan p = plan_skinny(M, N);
+  const long sk_rounds = (long(p.tiles_m) * p.tiles_n + 255) / 256;
+  const long tile_rounds = (tile_mx_tiles(M, N) + 255) / 256;
+  return sk_rounds * p.NT <= tile_rounds * 33;
+}
 
 hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
                          int M, int N, int K, hipStream_t stream) {

@@ -34,13 +34,7 @@
 //  * the slice's result, with the row's power of two undone, goes to Y (one
 //    slice) or to the slice's partial tile; small_reduce then adds the
 //    partials in slice order (deterministic).
-//
-// Looped form (kLoop, no workspace): one workgroup per (column group, row
-// chunk) walks every slice of K itself, adding each slice's unscaled result
-// to a running total in registers, in slice order, and stores Y once.  A
-// barrier separates a slice's last LDS reads from the next slice's copies.
-// This is the kernel behind w4a16_gemm_repacked for M > 4 (and for M <= 4
-// when the decode GEMV's LDS cannot hold the activation limbs).
+
 
 #include "w4a16_internal.h"
 #include "gemv_common.h"
@@ -90,7 +84,7 @@ __device__ __forceinline__ float sp_absmax(float4 a, float4 c) {
 // MB: 16-row blocks per row chunk.  Grid: CG column groups x RC row chunks x
 // S slices of sl steps (the last may be shorter); S4 steps in all.  Y when
 // S == 1, else the partials [S][M][N].
-template <int MB, bool kLoop>
+template <int MB>
 __global__ void __launch_bounds__(kSpThreads)
 small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const float *__restrict__ ps,
              float *__restrict__ Y, float *__restrict__ partial, int M, int N, int K, int tiles,
@@ -115,24 +109,8 @@ small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const fl
   const float *Xc = X + long(row0) * K;
   const int c16 = lane & 15;
   const int R = lane >> 4;
-  // looped form: the running total over slices, lane (c16, R) holding rows
-  // 16 i + 4 R + r of column 16 tile + c16 (as acc below)
-  float tot[kSpTW][MB][4];
-#pragma unroll
-  for (int j = 0; j < kSpTW; ++j)
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tot[j][i][r] = 0.0f;
-  const int zb = kLoop ? 0 : int(blockIdx.x / (CG * RC));
-  const int ze = kLoop ? S : zb + 1;
-  for (int z = zb; z < ze; ++z) {
-  if (kLoop && z > zb) {
-    // every wave has consumed its reads of the previous slice's image and
-    // exponents before any copy of this slice lands
-    sp_waitcnt<63, 0>();
-    sp_barrier();
-  }
+  const int z = int(blockIdx.x / (CG * RC));        // the slice of K
+  {
   const int st0 = z * sl;                           // first step of the slice
   const int jb0 = 16 * st0;                         // first 8-wide block of the slice
   const int jlim = std::min(16 * std::min(sl, S4 - st0), K8 - jb0);  // blocks inside slice and K
@@ -278,15 +256,7 @@ small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const fl
   }
 
   // lane (c16, R) holds rows 16 i + 4 R + r of column 16 tile + c16
-  if constexpr (kLoop) {
-#pragma unroll
-    for (int j = 0; j < kSpTW; ++j)
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tot[j][i][r] += ldexpf(acc[j][i][r], -rexp[16 * i + 4 * R + r]);
-  } else {
+  {
     float *out = S == 1 ? Y : partial + long(z) * M * N;
 #pragma unroll
     for (int j = 0; j < kSpTW; ++j) {
@@ -301,20 +271,6 @@ small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const fl
         }
     }
   }
-  }  // slices
-
-  if constexpr (kLoop) {
-#pragma unroll
-    for (int j = 0; j < kSpTW; ++j) {
-      const int n = (cg * kSpGroupTiles + wave * kSpTW + j) * 16 + c16;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * R + r;
-          if (row < Mw && n < N) Y[long(row0 + row) * N + n] = tot[j][i][r];
-        }
-    }
   }
 }
 
@@ -371,28 +327,13 @@ SmallPlan plan_small(int M, int N, int K) {
   return p;
 }
 
-template <int MB, bool kLoop>
+template <int MB>
 void run_small(const SmallPlan &p, const float *X, const uint4 *pw, const float *ps, float *Y,
                float *partial, int M, int N, int K, hipStream_t stream) {
-  const long blocks = long(p.CG) * p.RC * (kLoop ? 1 : p.S);
-  hipLaunchKernelGGL((small_packed<MB, kLoop>), dim3(unsigned(blocks)), dim3(kSpThreads),
+  const long blocks = long(p.CG) * p.RC * p.S;
+  hipLaunchKernelGGL((small_packed<MB>), dim3(unsigned(blocks)), dim3(kSpThreads),
                      size_t(sp_lds_bytes(MB)), stream, X, pw, ps, Y, partial, M, N, K, p.tiles,
                      p.S4, p.sl, p.CG, p.RC, p.S);
-}
-
-// The looped form's plan: row chunks of 16 rows (any M; the running totals
-// of 32-row chunks would not fit the registers), full slices of 8 steps
-// walked inside the workgroup.
-SmallPlan plan_small_loop(int M, int N, int K) {
-  SmallPlan p;
-  p.MB = 1;
-  p.RC = int((long(M) + 16 * p.MB - 1) / (16 * p.MB));
-  p.S4 = (K / kGroup + 3) / 4;
-  p.tiles = (N + 15) / 16;
-  p.CG = (p.tiles + kSpGroupTiles - 1) / kSpGroupTiles;
-  p.sl = std::min(kSpSteps, p.S4);
-  p.S = (p.S4 + p.sl - 1) / p.sl;
-  return p;
 }
 
 }  // namespace
@@ -414,9 +355,9 @@ hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int
   const float *ps = reinterpret_cast<const float *>(pw + long(p.tiles) * p.S4 * 64);
   float *partial = static_cast<float *>(workspace);
   if (p.MB == 1)
-    run_small<1, false>(p, X, pw, ps, Y, partial, M, N, K, stream);
+    run_small<1>(p, X, pw, ps, Y, partial, M, N, K, stream);
   else
-    run_small<2, false>(p, X, pw, ps, Y, partial, M, N, K, stream);
+    run_small<2>(p, X, pw, ps, Y, partial, M, N, K, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   const long total = long(M) * N;
@@ -427,17 +368,6 @@ hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int
     hipLaunchKernelGGL(small_reduce<false>, dim3(unsigned((total + 255) / 256)), dim3(256), 0,
                        stream, partial, Y, total, p.S);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_small_packed_loop(const float *X, const void *packed, float *Y, int M, int N,
-                                    int K, hipStream_t stream) {
-  if (M < 1) return hipErrorInvalidValue;
-  const SmallPlan p = plan_small_loop(M, N, K);
-  if (long(p.CG) * p.RC > 0x7fffffffL) return hipErrorInvalidValue;
-  const uint4 *pw = static_cast<const uint4 *>(packed);
-  const float *ps = reinterpret_cast<const float *>(pw + long(p.tiles) * p.S4 * 64);
-  run_small<1, true>(p, X, pw, ps, Y, nullptr, M, N, K, stream);
   return hipGetLastError();
 }
 

@@ -440,7 +440,7 @@ tile_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 
 }  // namespace
 
-long tile_mx_tiles(int M, int N) { return long((M + 127) / 128) * ((N + 127) / 128); }
+long tile_mx_tiles(int M, int N) { return ((long(M) + 127) / 128) * ((long(N) + 127) / 128); }
 
 hipError_t launch_tile_mx(const float *X, const int32_t *qweight, const float *scales, float *Y,
                           int M, int N, int K, hipStream_t stream) {

@@ -54,9 +54,7 @@ void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 int select_path(int64_t M, int64_t N, int64_t K) {
   (void)K;
-  if (M <= w4a16::kGemvMaxM) return W4A16_PATH_GEMV;
-  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  return tiles >= w4a16::kTileMxMinTiles ? W4A16_PATH_TILE_MX : W4A16_PATH_TILE;
+  return w4a16::skinny_preferred(int(M), int(N)) ? W4A16_PATH_GEMV : W4A16_PATH_TILE_MX;
 }
 
 }  // namespace
@@ -282,12 +280,10 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
     e = w4a16::launch_gemv_mfma_packed(X, packed, Y, int(M), int(N), int(K), s);
   else if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
     e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
-  else if (w4a16::skinny_supported(int(M)))
+  else if (w4a16::skinny_preferred(int(M), int(N)))
     e = w4a16::launch_skinny_repacked(X, packed, Y, int(M), int(N), int(K), s);
-  else if (w4a16::tile_mx_tiles(int(M), int(N)) >= w4a16::kTileMxMinTiles)
-    e = w4a16::launch_tile_mx_packed(X, packed, Y, int(M), int(N), int(K), s);
   else
-    e = w4a16::launch_small_packed_loop(X, packed, Y, int(M), int(N), int(K), s);
+    e = w4a16::launch_tile_mx_packed(X, packed, Y, int(M), int(N), int(K), s);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

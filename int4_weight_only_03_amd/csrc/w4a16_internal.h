@@ -35,11 +35,14 @@ hipError_t launch_gemv_mfma_swiglu(const float *X, const int32_t *qweight, const
 hipError_t launch_gemv_mfma_packed(const float *X, const void *packed, float *Y, int M, int N,
                                    int K, hipStream_t stream);
 
-// Skinny GEMM (1 <= M <= kSkinnyMaxM) on the fp16 matrix instructions: exact
-// weight codes, two fp16 limbs of each activation prescaled per row and pair
-// of groups, fp32 accumulation; no workspace.
-constexpr int kSkinnyMaxM = 64;
+// Skinny GEMM (any M >= 1) on the fp16 matrix instructions: exact weight
+// codes, two fp16 limbs of each activation prescaled per row and pair of
+// groups, fp32 accumulation; no workspace.  Up to kSkinnyAlwaysM rows it is
+// always the matrix-core choice; above, skinny_preferred(M, N) compares its
+// rounds of workgroups with the 128 x 128 tile's.
+constexpr int kSkinnyAlwaysM = 64;
 bool skinny_supported(int M);
+bool skinny_preferred(int M, int N);
 hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
                          int M, int N, int K, hipStream_t stream);
 // the skinny kernel on w4a16_repack's layout (one expert of the grouped pack)
@@ -53,12 +56,6 @@ hipError_t launch_tile(const float *X, const int32_t *qweight, const float *scal
 // of each activation (prescaled per row and pair of groups inside the kernel);
 // 128 x 128 tiles, no workspace.
 long tile_mx_tiles(int M, int N);
-// w4a16_gemm takes the matrix-core tile above 64 rows from this many 128 x 128
-// tiles on: one workgroup per CU, so a launch of fewer tiles leaves CUs idle
-// for the whole of K, where the fp32 tiled path's smaller tiles and K splits
-// fill the chip (measured on MI355X: even at 56-64 tiles, the matrix-core tile
-// ahead from 96)
-constexpr long kTileMxMinTiles = 96;
 hipError_t launch_tile_mx(const float *X, const int32_t *qweight, const float *scales, float *Y,
                           int M, int N, int K, hipStream_t stream);
 // the same kernel on the layout w4a16_repack writes (one expert of the grouped layout)
@@ -110,10 +107,6 @@ hipError_t launch_small_packed(const float *X, const void *packed, float *Y, int
 // on the current device (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(void **ptr);
-// the same GEMM for any M >= 1 with no workspace: each workgroup walks every
-// K slice of its (column group, row chunk) and adds the slices in order
-hipError_t launch_small_packed_loop(const float *X, const void *packed, float *Y, int M, int N,
-                                    int K, hipStream_t stream);
 // the packed layout of the grouped path: bytes, repack, the packed GEMM and
 // whether a shape can use it
 size_t grouped_pack_bytes(int E, int N, int K);
@@ -138,7 +131,5 @@ hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *
 hipError_t launch_read_floor(const void *const *ptrs, const long *bytes, int n, int threads,
                              int loads, unsigned *sink, hipStream_t stream);
 
-// Largest M the GEMV path (decode GEMVs and the skinny kernel) is chosen for.
-constexpr int kGemvMaxM = kSkinnyMaxM;
 
 }  // namespace w4a16

@@ -132,7 +132,7 @@ COHERENT = [
     (1, 64, K_MAX, ["auto", "split", "packed", "repacked", "small-packed"]),   # fp32 GEMV
     (2, 40, K_MAX, ["auto", "repacked"]),
     (9, 64, K_MAX, ["auto", "split", "repacked", "small-packed"]),             # skinny tiles
-    (130, 64, K_MAX, ["tile", "tile-mx"]),                                     # both tiles
+    (130, 64, K_MAX, ["auto", "tile", "tile-mx"]),             # skinny above 64 rows, both tiles
 ]
 
 

@@ -3,9 +3,9 @@ w4a16_repack must write the oracle's pack_grouped layout (one expert) byte for
 byte, and w4a16_gemm_repacked (the matrix-core decode GEMV of w4a16_gemm for
 M <= 8 and K <= 8192, bit for bit its result on the public layout; the
 split-K decode GEMV for M <= 4 with longer K when its LDS holds the
-activation limbs; the skinny kernel up to 64 rows; the 128 x 128 matrix-core
-tile above when the shape has at least 96 such tiles; the looped small-M
-kernel otherwise) must meet the tolerance on every output."""
+activation limbs; otherwise the skinny kernel or the 128 x 128 matrix-core
+tile, whichever w4a16_select_path picks) must meet the tolerance on every
+output."""
 
 import sys
 
@@ -63,10 +63,10 @@ SHAPES = [
     (5, 17, 32), (8, 100, 1056),
     # split-K decode GEMV (M <= 4, K > 8192, limbs fit its LDS)
     (1, 100, 38144), (4, 64, 9344),
-    # skinny kernel (K too long for the split-K decode kernel's LDS, or 9..64 rows)
+    # skinny kernel (K too long for the split-K decode kernel's LDS, 9..64 rows,
+    # and above 64 rows while its rounds cost less than the tile's)
     (1, 40, 38176), (4, 20, 9376), (17, 70, 160), (33, 45, 4128), (63, 33, 96), (64, 300, 7168),
-    # looped small-M kernel above 64 rows with few tiles
-    (65, 129, 224), (130, 200, 320), (300, 260, 256),
+    (65, 129, 224), (130, 200, 320), (300, 260, 256), (1100, 1300, 32),
 ]
 
 
@@ -152,17 +152,18 @@ def test_repacked_nonfinite_row(dev):
     assert oracle.compare(Y[keep], X[keep], qw, sc)["ok"]
 
 
-# the 128 x 128 matrix-core tile on repacked weights (M > 64, at least 96 tiles):
-# ragged M and N (rows padded to 16 in the layout, trailing tiles clamped), odd
-# group counts (steps padded to 4 groups), and the workload sizes' K
-TILE_SHAPES = [(1300, 1200, 160), (1200, 1290, 2080), (1025, 1536, 7168), (1100, 1300, 32),
-               (1664, 1032, 96)]
+# the 128 x 128 matrix-core tile on repacked weights (shapes w4a16_select_path
+# gives to it): ragged M and N (rows padded to 16 in the layout, trailing tiles
+# clamped), odd group counts (steps padded to 4 groups), and the workload
+# sizes' K
+TILE_SHAPES = [(2100, 1200, 160), (2200, 1290, 2080), (1700, 1600, 7168), (2300, 1300, 32),
+               (2688, 1032, 96)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
 def test_repacked_tile_shapes(dev, M, N, K):
     say(f"repacked tile M={M} N={N} K={K}")
-    assert -(-M // 128) * -(-N // 128) >= 96
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE_MX
     X, W = workloads.random_case(M, N, K, seed=M + 7 * N + K)
     qw, sc = oracle.quantize(W)
     v = oracle.compare(run(X, qw, sc, dev), X, qw, sc)
@@ -171,7 +172,8 @@ def test_repacked_tile_shapes(dev, M, N, K):
 
 
 def test_repacked_tile_integer_exact(dev):
-    M, N, K = 1100, 1300, 288
+    M, N, K = 2300, 1300, 288
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE_MX
     rng = np.random.default_rng(31)
     X = rng.integers(-8, 9, (M, K)).astype(np.float32)
     nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
@@ -182,10 +184,11 @@ def test_repacked_tile_integer_exact(dev):
 
 
 def test_repacked_tile_guard_band_and_nonfinite(dev):
-    M, N, K = 1100, 1300, 224
+    M, N, K = 2300, 1300, 224
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE_MX
     X, W = workloads.random_case(M, N, K, seed=14)
     X[3, 17] = np.inf
-    X[1099, 200] = np.nan
+    X[2299, 200] = np.nan
     qw, sc = oracle.quantize(W)
     pad = 4096
     buf = torch.full((pad + M * N + pad,), 0x7FC0DEAD, dtype=torch.int32, device=dev)
@@ -193,8 +196,8 @@ def test_repacked_tile_guard_band_and_nonfinite(dev):
     a = run(X, qw, sc, dev, Y)
     host = buf.cpu().numpy().view(np.uint32)
     assert np.all(host[:pad] == 0x7FC0DEAD) and np.all(host[pad + M * N:] == 0x7FC0DEAD)
-    assert not np.any(np.isfinite(a[3])) and not np.any(np.isfinite(a[1099]))
-    keep = [m for m in range(M) if m not in (3, 1099)]
+    assert not np.any(np.isfinite(a[3])) and not np.any(np.isfinite(a[2299]))
+    keep = [m for m in range(M) if m not in (3, 2299)]
     assert oracle.compare(a[keep], X[keep], qw, sc)["ok"]
     # the same bits as the public layout's matrix-core tile
     pub = binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev),

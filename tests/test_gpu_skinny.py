@@ -1,6 +1,7 @@
-"""GPU parity of the skinny matrix-core kernel (W4A16_GEMV_SKINNY: 3 <= M <= 64
+"""GPU parity of the skinny matrix-core kernel (W4A16_GEMV_SKINNY: M >= 3
 outside the decode GEMV's range), the kernel w4a16_gemm runs for the
-tree-verification batches, against the CPU oracle through the C ABI."""
+tree-verification batches and, above 64 rows, while its rounds cost less than
+the 128 x 128 tile's, against the CPU oracle through the C ABI."""
 
 import sys
 
@@ -61,6 +62,51 @@ def test_shapes_against_oracle(dev, M, N, K):
     X, W = workloads.random_case(M, N, K, seed=M * 131 + N * 7 + K)
     qw, sc = oracle.quantize(W)
     check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+
+
+# above 64 rows: one to many row blocks, the last one ragged; NT = 4, 2 and 1
+# column tiles per workgroup (N from 33 to 4096); group counts past and short
+# of a whole step
+WIDE = [(65, 300, 2080), (65, 2048, 224), (80, 4096, 96), (130, 129, 224), (300, 260, 256), (513, 70, 4128),
+        (1000, 33, 160), (777, 1030, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE)
+def test_above_64_rows_every_output(dev, M, N, K):
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_GEMV
+    say(f"skinny M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M * 17 + N + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+
+
+def test_forced_where_the_tile_wins(dev):
+    # 600 x 4096: the automatic choice is the matrix-core tile; the GEMV path
+    # forced runs the skinny kernel at this M as well
+    M, N, K = 600, 4096, 96
+    assert binding.w4a16_select_path(M, N, K) == binding.W4A16_PATH_TILE_MX
+    X, W = workloads.random_case(M, N, K, seed=600)
+    qw, sc = oracle.quantize(W)
+    Y = binding.w4a16_gemm_path(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev),
+                                path=binding.W4A16_PATH_GEMV)
+    torch.cuda.synchronize()
+    check(Y.cpu().numpy(), X, qw, sc, "skinny forced 600x4096x96")
+
+
+def test_above_64_rows_integer_exact_and_nonfinite(dev):
+    M, N, K = 200, 130, 512
+    X, nib = workloads.integer_case(M, N, K, seed=5)
+    qw = oracle.pack(nib)
+    sc = np.full((N, K // 32), np.float32(0.25), dtype=np.float32)
+    Y = run(X, qw, sc, dev)
+    assert np.array_equal(Y.astype(np.float64), oracle.gemm(X, qw, sc))
+    X[70, 3] = np.inf
+    X[199, 500] = np.nan
+    Y = run(X, qw, sc, dev)
+    assert np.all(np.isnan(Y[70])) and np.all(np.isnan(Y[199]))
+    keep = [m for m in range(M) if m not in (70, 199)]
+    assert np.array_equal(Y[keep].astype(np.float64), oracle.gemm(X[keep], qw, sc))
 
 
 @pytest.mark.parametrize("M", [3, 5, 8])

@@ -74,14 +74,14 @@ def test_grids_with_and_without_the_xcd_order(dev, M, N, K):
 
 
 def test_auto_dispatch_reaches_it(dev):
-    M, N, K = 257, 4096, 256
+    M, N, K = 513, 4096, 256
     assert binding.w4a16_select_path(M, N, K) == TMX
     X, W = workloads.random_case(M, N, K, seed=5)
     qw, sc = oracle.quantize(W)
     Y = binding.w4a16_gemm(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev))
     torch.cuda.synchronize()
     a = Y.cpu().numpy()
-    check(a, X, qw, sc, "tile-mx auto 257x4096x256")
+    check(a, X, qw, sc, "tile-mx auto 513x4096x256")
     assert np.array_equal(a.view(np.uint32), run(X, qw, sc, dev).view(np.uint32))
 
 
@@ -164,20 +164,22 @@ def test_same_as_fp32_tile_within_tolerance(dev):
     check(run(X, qw, sc, dev, path=binding.W4A16_PATH_TILE), X, qw, sc, "tile 384x512x2048")
 
 
-@pytest.mark.parametrize("N,want", [(12161, binding.W4A16_PATH_TILE_MX), (12160, binding.W4A16_PATH_TILE)])
-def test_dispatch_boundary_every_output(dev, N, want):
-    # 65 rows: the smallest M above the GEMV path, one 128-row tile with 63
-    # padded rows; 96 tiles of 128 x 128 take the matrix-core tile (N ragged),
-    # 95 the fp32 tile; w4a16_gemm and, for the matrix-core tile, the repacked
-    # entry point on the same weights
-    M, K = 65, 96
+@pytest.mark.parametrize("M,want", [(513, binding.W4A16_PATH_TILE_MX), (512, binding.W4A16_PATH_GEMV)])
+def test_dispatch_boundary_every_output(dev, M, want):
+    # N = 4096: 512 rows are the last the skinny kernel takes (8 rounds of
+    # 256 workgroups x 4 against one round of tiles x 33); 513 rows go to the
+    # matrix-core tile, one 128-row tile with 127 padded rows; w4a16_gemm and
+    # the repacked entry point on the same weights (bit for bit on the tile)
+    N, K = 4096, 96
     assert binding.w4a16_select_path(M, N, K) == want
-    X, W = workloads.random_case(M, N, K, seed=N)
+    X, W = workloads.random_case(M, N, K, seed=M)
     qw, sc = oracle.quantize(W)
     Y = run(X, qw, sc, dev, path=binding.W4A16_PATH_AUTO)
     check(Y, X, qw, sc, f"w4a16_gemm M={M} N={N}")
+    packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
+    Yr = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, N)
+    torch.cuda.synchronize()
+    Yr = Yr.cpu().numpy()
+    check(Yr, X, qw, sc, f"w4a16_gemm_repacked M={M} N={N}")
     if want == binding.W4A16_PATH_TILE_MX:
-        packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
-        Yr = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, N)
-        torch.cuda.synchronize()
-        assert np.array_equal(Yr.cpu().numpy().view(np.uint32), Y.view(np.uint32))
+        assert np.array_equal(Yr.view(np.uint32), Y.view(np.uint32))

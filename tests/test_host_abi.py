@@ -43,8 +43,7 @@ def test_status_strings(lib):
 
 def test_gemv_kernel(lib):
     # matrix-core decode GEMV for M <= 8 and K <= 8192; the skinny matrix-core
-    # kernel for 3 <= M <= 64 otherwise; the fp32 FMA GEMV for M <= 2 with long K
-    # (and for M > 64 forced onto the GEMV path)
+    # kernel for M >= 3 otherwise; the fp32 FMA GEMV for M <= 2 with long K
     assert binding.w4a16_gemv_kernel(1, 4096, 7168) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(2, 7, 8192) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_FMA
@@ -54,25 +53,51 @@ def test_gemv_kernel(lib):
     assert binding.w4a16_gemv_kernel(8, 64, 256) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(9, 64, 256) == binding.W4A16_GEMV_SKINNY
     assert binding.w4a16_gemv_kernel(64, 4096, 7168) == binding.W4A16_GEMV_SKINNY
-    assert binding.w4a16_gemv_kernel(65, 64, 256) == binding.W4A16_GEMV_FMA
+    assert binding.w4a16_gemv_kernel(65, 64, 256) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(4096, 4096, 7168) == binding.W4A16_GEMV_SKINNY
     assert binding.w4a16_gemv_kernel(0, 64, 256) == 0
     assert binding.w4a16_gemv_kernel(1, 64, 250) == 0
     assert binding.w4a16_gemv_kernel(1, 0, 256) == 0
 
 
+def skinny_cost(M, N):
+    # rounds of 256 workgroups of 16 x 16 NT outputs, NT the widest of 4, 2, 1
+    # that leaves at least 256 workgroups, each weighted by NT
+    tm = -(-M // 16)
+    nt = next((t for t in (4, 2) if -(-N // (16 * t)) * tm >= 256), 1)
+    return -(-(tm * -(-N // (16 * nt))) // 256) * nt
+
+
+def tile_cost(M, N):
+    # rounds of 256 tiles of 128 x 128, each weighted by 33
+    return -(-(-(-M // 128) * -(-N // 128)) // 256) * 33
+
+
 def test_select_path(lib):
-    # the decode/verify path for M <= 64; above, the matrix-core tile from 96
-    # tiles of 128 x 128 on, the fp32 tiled path below
+    # the decode/verify path for M <= 64; above, the skinny kernel (still the
+    # GEMV path) while its weighted rounds cost no more than the matrix-core
+    # tile's; the fp32 tiled path is never the automatic choice
+    GEMV, TMX = binding.W4A16_PATH_GEMV, binding.W4A16_PATH_TILE_MX
     for M in (1, 4, 5, 8, 9, 17, 64):
-        assert binding.w4a16_select_path(M, 4096, 7168) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(5, 4096, 8192 + 32) == binding.W4A16_PATH_GEMV
-    assert binding.w4a16_select_path(65, 4096, 7168) == binding.W4A16_PATH_TILE      # 32 tiles
-    assert binding.w4a16_select_path(256, 4096, 7168) == binding.W4A16_PATH_TILE     # 64 tiles
-    assert binding.w4a16_select_path(257, 4096, 7168) == binding.W4A16_PATH_TILE_MX  # 96 tiles
-    assert binding.w4a16_select_path(65, 12161, 7168) == binding.W4A16_PATH_TILE_MX  # 96
-    assert binding.w4a16_select_path(65, 12160, 7168) == binding.W4A16_PATH_TILE     # 95
-    assert binding.w4a16_select_path(4096, 4096, 7168) == binding.W4A16_PATH_TILE_MX
-    assert binding.w4a16_select_path(1 << 24, 1 << 30, 32) == binding.W4A16_PATH_TILE_MX
+        assert binding.w4a16_select_path(M, 4096, 7168) == GEMV
+    assert binding.w4a16_select_path(5, 4096, 8192 + 32) == GEMV
+    # N = 4096: 512 rows cost 8 skinny rounds x 4 = 32 <= 33; 513 rows 9 x 4 = 36
+    for M, want in ((65, GEMV), (256, GEMV), (257, GEMV), (512, GEMV), (513, TMX),
+                    (4096, TMX)):
+        assert binding.w4a16_select_path(M, 4096, 7168) == want, M
+    # N = 14336: 144 rows cost 8 x 4 = 32, 145 rows 9 x 4 = 36, against one
+    # round of 224 tiles
+    assert binding.w4a16_select_path(144, 14336, 4096) == GEMV
+    assert binding.w4a16_select_path(145, 14336, 4096) == TMX
+    # narrow N: the skinny kernel at every M measured
+    assert binding.w4a16_select_path(768, 2048, 7168) == GEMV
+    assert binding.w4a16_select_path(65, 12161, 7168) == GEMV
+    assert binding.w4a16_select_path(1 << 24, 1 << 30, 32) == TMX
+    # the rule itself over a grid of shapes
+    for M in (65, 100, 128, 200, 300, 500, 1000, 3000):
+        for N in (16, 100, 1024, 3000, 7168, 20000):
+            want = GEMV if skinny_cost(M, N) <= tile_cost(M, N) else TMX
+            assert binding.w4a16_select_path(M, N, 4096) == want, (M, N)
 
 
 # ------------------------------------------------------------------ quantize
