@@ -35,7 +35,6 @@
 //    slice) or to the slice's partial tile; small_reduce then adds the
 //    partials in slice order (deterministic).
 
-
 #include "w4a16_internal.h"
 #include "gemv_common.h"
 #include "limbs.h"
@@ -110,7 +109,6 @@ small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const fl
   const int c16 = lane & 15;
   const int R = lane >> 4;
   const int z = int(blockIdx.x / (CG * RC));        // the slice of K
-  {
   const int st0 = z * sl;                           // first step of the slice
   const int jb0 = 16 * st0;                         // first 8-wide block of the slice
   const int jlim = std::min(16 * std::min(sl, S4 - st0), K8 - jb0);  // blocks inside slice and K
@@ -256,21 +254,18 @@ small_packed(const float *__restrict__ X, const uint4 *__restrict__ pw, const fl
   }
 
   // lane (c16, R) holds rows 16 i + 4 R + r of column 16 tile + c16
-  {
-    float *out = S == 1 ? Y : partial + long(z) * M * N;
+  float *out = S == 1 ? Y : partial + long(z) * M * N;
 #pragma unroll
-    for (int j = 0; j < kSpTW; ++j) {
-      const int n = (cg * kSpGroupTiles + wave * kSpTW + j) * 16 + c16;
+  for (int j = 0; j < kSpTW; ++j) {
+    const int n = (cg * kSpGroupTiles + wave * kSpTW + j) * 16 + c16;
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * R + r;
-          if (row < Mw && n < N)
-            out[long(row0 + row) * N + n] = ldexpf(acc[j][i][r], -rexp[row]);
-        }
-    }
-  }
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * i + 4 * R + r;
+        if (row < Mw && n < N)
+          out[long(row0 + row) * N + n] = ldexpf(acc[j][i][r], -rexp[row]);
+      }
   }
 }
 
