@@ -376,7 +376,9 @@ int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K);
  * leaves at least 256 workgroups) against ceil(ceil(M/128) * ceil(N/128) / 256)
  * * 33 for the tile, the skinny kernel on a tie.  The fp32 tiled path
  * (W4A16_PATH_TILE) is no longer chosen: the skinny kernel is about twice as
- * fast on every shape where the tile does not win.  Host only; no GPU use. */
+ * fast on every shape where the tile does not win.  For M or N <= 0 (no-ops)
+ * the GEMV path, for M or N beyond W4A16_MAX_M / W4A16_MAX_N (refused by the
+ * GEMM) the tile.  Host only; no GPU use. */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 
 /*

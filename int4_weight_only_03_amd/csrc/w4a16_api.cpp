@@ -54,6 +54,8 @@ void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 int select_path(int64_t M, int64_t N, int64_t K) {
   (void)K;
+  if (M <= 0 || N <= 0) return W4A16_PATH_GEMV;  // no-op shapes: nothing runs
+  if (M > W4A16_MAX_M || N > W4A16_MAX_N) return W4A16_PATH_TILE_MX;  // refused by the GEMM
   return w4a16::skinny_preferred(int(M), int(N)) ? W4A16_PATH_GEMV : W4A16_PATH_TILE_MX;
 }
 

@@ -93,6 +93,10 @@ def test_select_path(lib):
     assert binding.w4a16_select_path(768, 2048, 7168) == GEMV
     assert binding.w4a16_select_path(65, 12161, 7168) == GEMV
     assert binding.w4a16_select_path(1 << 24, 1 << 30, 32) == TMX
+    # extents the GEMM refuses or treats as no-ops still get an answer
+    assert binding.w4a16_select_path(0, 4096, 7168) == GEMV
+    assert binding.w4a16_select_path(1 << 40, 4096, 7168) == TMX
+    assert binding.w4a16_select_path(4096, 1 << 40, 7168) == TMX
     # the rule itself over a grid of shapes
     for M in (65, 100, 128, 200, 300, 500, 1000, 3000):
         for N in (16, 100, 1024, 3000, 7168, 20000):
