@@ -83,7 +83,7 @@ PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common
                 "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
-                "repacked": ["gemv_mfma.hip", "packed_gemv.hip", "skinny.hip", "tile_mx.hip",
+                "repacked": ["gemv_mfma.hip", "skinny.hip", "tile_mx.hip",
                              "small_packed.hip", "gemv_common.h", "limbs.h"],
                 "small-packed": ["small_packed.hip", "gemv_common.h", "limbs.h"],
                 "read-floor": ["read_floor.hip", "gemv_common.h"]}

@@ -86,8 +86,8 @@ extern "C" {
 #define W4A16_PATH_SPLIT 3    /* split-precision path (w4a16_gemm_split only): fp16 MFMA on
                                  exact (q - 8) codes and two fp16 limbs of each activation */
 #define W4A16_PATH_GEMV_FMA 4 /* the fp32 FMA GEMV kernels for any M and K: one fp32 FMA per
-                                 weight with the activations in VGPRs (the GEMV path's kernel
-                                 for K > 8192); for measurement beside the matrix-core GEMV */
+                                 weight with the activations in VGPRs; for measurement beside
+                                 the matrix-core GEMV (never the automatic choice) */
 #define W4A16_PATH_TILE_MX 5  /* large-M matrix-core tile: fp16 MFMA 16x16x32 on exact (q - 8)
                                  codes and two fp16 limbs of each activation, prescaled by a
                                  power of two per row and pair of groups inside the kernel
@@ -168,12 +168,10 @@ int w4a16_repack(const int32_t *qweight, const float *scales, void *packed, int6
                  int64_t K, int32_t group, void *stream);
 
 /* Y[M][N] = X[M][K] . dequant(W)^T with W repacked by w4a16_repack(..., N, K,
- * ...).  No workspace and no allocation: for M <= 8 and K <= 8192 the decode
- * GEMV of W4A16_GEMV_MFMA, each lane gathering its group's 16 bytes from four
- * repacked chunks (bit for bit the result of w4a16_gemm on the public
- * layout); for M <= 4 with longer K (when the activation limbs fit the
- * kernel's LDS) a decode GEMV whose workgroups split K over their waves, with
- * the arithmetic of w4a16_gemm_split (limbs prescaled per row); otherwise,
+ * ...).  No workspace and no allocation: where w4a16_gemv_kernel picks
+ * W4A16_GEMV_MFMA, that decode GEMV, each lane gathering its group's 16 bytes
+ * from four repacked chunks (bit for bit the result of w4a16_gemm on the
+ * public layout); otherwise,
  * where w4a16_select_path picks the GEMV path, the kernel of W4A16_GEMV_SKINNY
  * reading the repacked blocks whole (limbs prescaled per row and pair of
  * groups, low limb x2^11), and where it picks W4A16_PATH_TILE_MX that
@@ -198,8 +196,8 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
  *     silu(g) = g / (1 + exp(-g)),
  * with g and u the same fp32 group-scaled sums as w4a16_gemm and the epilogue
  * in fp32.  Y is [M][F] (not 2F); the gate/up outputs never reach memory.
- * Runs on the GEMV kernels (the matrix-core one for M <= 8 and K <= 8192,
- * w4a16_gemv_kernel; any M accepted).  Errors as
+ * Runs on the matrix-core decode GEMV for M <= 8 and on the fp32 FMA GEMV
+ * above (any M accepted; the skinny kernel has no fused form).  Errors as
  * w4a16_gemm with N = 2F.
  */
 int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scales, float *Y,
@@ -343,7 +341,9 @@ int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
 
 /* Kernels behind W4A16_PATH_GEMV. */
-#define W4A16_GEMV_MFMA 1     /* M <= 8, K <= 8192: v_mfma_f32_4x4x4_16b_f16 on exact weight
+#define W4A16_GEMV_MFMA 1     /* M <= 4, and 5 <= M <= 8 unless N >= 4096 and K >= 4096 (any
+                                 K; beyond 8192, 8 waves take blocks of 16 groups in turn):
+                                 v_mfma_f32_4x4x4_16b_f16 on exact weight
                                  codes (nibble - 8) and two fp16 limbs of each activation; every
                                  group of 32 activations is scaled by a power of two (max |x|
                                  into [2^14, 2^15)) before the split, so the limbs hold 22
@@ -351,9 +351,11 @@ int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
                                  group's maximum (the low limb carried x2^11); products exact
                                  in fp32, fp32 accumulation, one fp32 multiply per (row,
                                  group) applies scale * 2^-e */
-#define W4A16_GEMV_FMA 2      /* M <= 2 with K > 8192: one fp32 FMA per weight, activations
-                                 in VGPRs */
-#define W4A16_GEMV_SKINNY 3   /* M >= 3 otherwise (the tree-verification batches and beyond):
+#define W4A16_GEMV_FMA 2      /* the fp32 FMA GEMV (one fp32 FMA per weight, activations in
+                                 VGPRs): no longer returned for any shape; it runs under
+                                 W4A16_PATH_GEMV_FMA */
+#define W4A16_GEMV_SKINNY 3   /* M >= 9 (the tree-verification batches and beyond), and
+                                 5 <= M <= 8 when N >= 4096 and K >= 4096:
                                  v_mfma_f32_16x16x32_f16 on exact weight codes and two fp16
                                  limbs of each activation, prescaled by a power of two per
                                  row and pair of groups, the low limb x2^11 and met by the

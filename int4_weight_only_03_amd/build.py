@@ -21,7 +21,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["gemv.hip", "gemv_mfma.hip", "tile.hip", "split.hip", "grouped.hip", "packed_gemv.hip",
+DEVICE_SOURCES = ["gemv.hip", "gemv_mfma.hip", "tile.hip", "split.hip", "grouped.hip",
                   "small_packed.hip", "read_floor.hip", "skinny.hip", "tile_mx.hip"]
 HOST_SOURCES = ["w4a16_api.cpp", "w4a16_io.cpp"]
 # per-source options: the split path's MFMA results stay in VGPRs (the scale

@@ -422,15 +422,24 @@ hipError_t launch(const float *X, const int32_t *qweight, const float *scales, f
 
 }  // namespace
 
-int gemv_kernel(int M, int K) {
-  if (gemv_mfma_supported(M, K)) return W4A16_GEMV_MFMA;  // matrix-core decode GEMV
+// From 5 rows the decode GEMV carries four A operands per weight word (8
+// rows' limbs), and on a weight matrix of at least 4096 x 4096 the skinny
+// kernel, which then fills the chip with 16-row tiles, is the faster one
+// (measured on MI355X: 13.0 against 17.4 us at 8 x 4096 x 7168, 20.1 against
+// 24.9 at 8 x 14336 x 4096; below that size the two are even or the GEMV
+// wins, 9.5 against 11.7 us at 8 x 1024 x 7168).
+bool skinny_beats_decode_gemv(int M, int N, int K) { return M >= 5 && N >= 4096 && K >= 4096; }
+
+int gemv_kernel(int M, int N, int K) {
+  if (gemv_mfma_supported(M, K) && !skinny_beats_decode_gemv(M, N, K))
+    return W4A16_GEMV_MFMA;  // matrix-core decode GEMV
   if (M >= 3 && skinny_supported(M)) return W4A16_GEMV_SKINNY;  // skinny.hip
   return W4A16_GEMV_FMA;
 }
 
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream) {
-  switch (gemv_kernel(M, K)) {
+  switch (gemv_kernel(M, N, K)) {
     case W4A16_GEMV_MFMA: return launch_gemv_mfma(X, qweight, scales, Y, M, N, K, stream);
     case W4A16_GEMV_SKINNY: return launch_skinny(X, qweight, scales, Y, M, N, K, stream);
     default: return launch<false>(X, qweight, scales, Y, M, N, K, stream);

@@ -44,8 +44,10 @@
 // last valid byte (the activation row at K, the workgroup's weights and
 // scales at row N): rows past N and groups past K read zero, with no clamped
 // addresses or selects, and each load's address is one 32-bit offset.  One
-// workgroup covers 4R rows and all groups (one wave per 16 groups,
-// K <= 8192), about one workgroup per compute unit.
+// workgroup covers 4R rows and all groups (one wave per 16 groups up to
+// K = 8192; beyond, 16 waves taking blocks of 16 groups in turn, one pass of
+// loads, split and products per block), about one workgroup per compute
+// unit.
 
 #include "w4a16_internal.h"
 #include "gemv_common.h"
@@ -58,7 +60,8 @@ namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMxMaxGroups = 256;  // 16 waves of 16 groups: K <= 8192
+constexpr int kMxMaxWaves = 16;   // one pass of 16 groups each: K <= 8192
+constexpr int kMxLongWaves = 8;   // longer K: passes of 8 blocks of 16 groups (256 VGPRs a wave)
 // word 3 of a raw buffer resource (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -82,7 +85,7 @@ static_assert(mx_wave_lds(8) >= 8 * 4 * 4 * sizeof(float), "partials fit the lim
 // each lane gathers the same 16 bytes (words 0..3 of its group and row) from
 // four chunks 256 bytes apart, so the arithmetic and its result are those of
 // the public layout, bit for bit.
-template <int MT, int R, bool kSw, bool kPk>
+template <int MT, int R, bool kSw, bool kPk, bool kLong>
 __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint4 *__restrict__ qw,
                                         const float *__restrict__ sc, float *const (&yr)[MT],
                                         int N, int G, long rowbase, unsigned char *smem, int S4,
@@ -93,7 +96,14 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int b = lane >> 2, j = lane & 3;
-  const int g = wave * 16 + b;
+  // kLong (K beyond 16 waves of 16 groups): the waves take blocks of 16
+  // groups in turn, block wave + nw * it in pass it, each pass's sums adding
+  // into acc; otherwise one pass.
+  const int nw = int(blockDim.x >> 6);
+  const int passes = kLong ? (G + 16 * nw - 1) / (16 * nw) : 1;
+  float acc[MT][RL];
+  for (int it = 0; it < passes; ++it) {
+  const int g = (wave + nw * it) * 16 + b;
   const bool gv = g < G;
 
   // Buffer loads: a workgroup's weight rows start its buffers, which end at
@@ -204,7 +214,6 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
     if (p + 1 < MS) __builtin_amdgcn_wave_barrier();  // the next operand's writes stay behind
   }
 
-  float acc[MT][RL];
 #pragma unroll
   for (int q = 0; q < RL; ++q) {
     const uint32_t u[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
@@ -231,10 +240,12 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
         const int m = 2 * p + h;
         if (m < MT) {
           const float sp = s[q] * inv[m];  // exact: a power-of-two factor
-          acc[m][q] = sp * fmaf(d[p][2 * h + 1], 0x1p-11f, d[p][2 * h]);
+          const float v = sp * fmaf(d[p][2 * h + 1], 0x1p-11f, d[p][2 * h]);
+          acc[m][q] = it == 0 ? v : acc[m][q] + v;
         }
       }
   }
+  }  // passes
 
   // sum over the wave's groups: lanes with equal j
   float *red = reinterpret_cast<float *>(smem + wave * mx_wave_lds(MT));  // this wave's own region
@@ -267,8 +278,8 @@ __device__ __forceinline__ void mx_pass(const float *const (&xr)[MT], const uint
 
 // N: outputs per row of Y (F for kSw, whose W has 2N rows).  MT = 4 serves
 // M = 3 and 4, MT = 8 serves M = 5 .. 8.
-template <int MT, int R, bool kSw, bool kPk>
-__global__ void __launch_bounds__(1024)
+template <int MT, int R, bool kSw, bool kPk, bool kLong>
+__global__ void __launch_bounds__(kLong ? 64 * kMxLongWaves : 64 * kMxMaxWaves)
 gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
         float *__restrict__ Y, int M, int N, int G, int S4, long T16) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -280,19 +291,25 @@ gemv_mx(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
     xr[m] = X + (m < M ? m : 0) * K;
     yr[m] = m < M ? Y + long(m) * N : nullptr;
   }
-  mx_pass<MT, R, kSw, kPk>(xr, qw, sc, yr, N, G, long(blockIdx.x) * (4 * R), smem, S4, T16);
+  mx_pass<MT, R, kSw, kPk, kLong>(xr, qw, sc, yr, N, G, long(blockIdx.x) * (4 * R), smem, S4, T16);
 }
 
 template <int MT, int R, bool kSw, bool kPk>
 hipError_t run_mx(const float *X, const void *qw, const float *sc, float *Y, int M, int N,
                   int G, hipStream_t stream) {
-  const int waves = (G + 15) / 16;
+  const bool lng = G > 16 * kMxMaxWaves;
+  const int waves = lng ? kMxLongWaves : (G + 15) / 16;
   const int blocks = int((long(N) + 4 * R - 1) / (4 * R));
   const int S4 = (G + 3) / 4;
   const long T16 = (long(N) + 15) / 16;
-  hipLaunchKernelGGL((gemv_mx<MT, R, kSw, kPk>), dim3(blocks), dim3(waves * 64),
-                     waves * mx_wave_lds(MT), stream, X, reinterpret_cast<const uint4 *>(qw), sc,
-                     Y, M, N, G, S4, T16);
+  if (lng)
+    hipLaunchKernelGGL((gemv_mx<MT, R, kSw, kPk, true>), dim3(blocks), dim3(waves * 64),
+                       waves * mx_wave_lds(MT), stream, X, reinterpret_cast<const uint4 *>(qw), sc,
+                       Y, M, N, G, S4, T16);
+  else
+    hipLaunchKernelGGL((gemv_mx<MT, R, kSw, kPk, false>), dim3(blocks), dim3(waves * 64),
+                       waves * mx_wave_lds(MT), stream, X, reinterpret_cast<const uint4 *>(qw), sc,
+                       Y, M, N, G, S4, T16);
   return hipGetLastError();
 }
 
@@ -320,7 +337,7 @@ hipError_t dispatch_mx(int R, const float *X, const void *qw, const float *sc, f
 }  // namespace
 
 bool gemv_mfma_supported(int M, int K) {
-  return M >= 1 && M <= 8 && K / kGroup <= kMxMaxGroups;
+  return M >= 1 && M <= 8 && K >= kGroup;
 }
 
 // Quads of rows per lane: the most that still leaves at least 224 workgroups

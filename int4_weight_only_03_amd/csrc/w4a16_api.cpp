@@ -278,10 +278,8 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
   clear_stale_hip_error();
 
   hipError_t e;
-  if (w4a16::gemv_mfma_supported(int(M), int(K)))
+  if (w4a16::gemv_kernel(int(M), int(N), int(K)) == W4A16_GEMV_MFMA)
     e = w4a16::launch_gemv_mfma_packed(X, packed, Y, int(M), int(N), int(K), s);
-  else if (M <= 4 && w4a16::decode_packed_supported(int(M), int(K)))
-    e = w4a16::launch_decode_packed(X, packed, Y, int(M), int(N), int(K), s);
   else if (w4a16::skinny_preferred(int(M), int(N)))
     e = w4a16::launch_skinny_repacked(X, packed, Y, int(M), int(N), int(K), s);
   else
@@ -349,7 +347,7 @@ int w4a16_gemm_small_packed_noalloc(const float *X, const void *packed, float *Y
 int w4a16_gemv_kernel(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % W4A16_GROUP != 0) return 0;
   if (M > W4A16_MAX_M || N > W4A16_MAX_N || K > W4A16_MAX_K) return 0;
-  return w4a16::gemv_kernel(int(M), int(K));
+  return w4a16::gemv_kernel(int(M), int(N), int(K));
 }
 
 int w4a16_grouped_kernel(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {

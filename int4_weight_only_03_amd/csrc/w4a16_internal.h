@@ -17,10 +17,10 @@ constexpr int kGroup = 32;
 hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scales, float *Y,
                        int M, int N, int K, hipStream_t stream);
 
-// The kernel launch_gemv runs for M rows and K (one of W4A16_GEMV_*).
-int gemv_kernel(int M, int K);
+// The kernel launch_gemv runs for an M x N x K shape (one of W4A16_GEMV_*).
+int gemv_kernel(int M, int N, int K);
 
-// Decode GEMV (M <= 8, K <= 8192) on the 4x4x4 fp16 matrix instructions:
+// Decode GEMV (M <= 8, any K) on the 4x4x4 fp16 matrix instructions:
 // exact weight codes, two fp16 limbs of each group-prescaled activation.
 // launch_gemv runs it whenever gemv_mfma_supported(M, K).
 bool gemv_mfma_supported(int M, int K);
@@ -92,10 +92,7 @@ hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const floa
 // which kernel launch_grouped runs for this shape: 1 matrix cores, 2 fp32
 // FMA with staged token rows, 3 fp32 FMA reading activations from memory
 int grouped_kernel(int T, int R, int E, int N, int K);
-// decode GEMV (M <= 4) on weights packed by the grouped repack (one expert)
-bool decode_packed_supported(int M, int K);
-hipError_t launch_decode_packed(const float *X, const void *packed, float *Y, int M, int N, int K,
-                                hipStream_t stream);
+
 // small-M GEMM (1 <= M <= 64) on weights packed by the grouped repack (one
 // expert); workspace: the split-K partials (0 bytes when K is not split)
 bool small_packed_supported(int M);

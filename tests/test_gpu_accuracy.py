@@ -129,7 +129,7 @@ COHERENT = [
     (1, 256, 7168, ["auto", "split", "repacked"]),          # matrix-core decode GEMV
     (8, 100, 8192, ["auto", "small-packed"]),               # its longest K, 8 rows
     (64, 256, 7168, ["auto", "split", "packed", "repacked", "small-packed"]),  # skinny tiles
-    (1, 64, K_MAX, ["auto", "split", "packed", "repacked", "small-packed"]),   # fp32 GEMV
+    (1, 64, K_MAX, ["auto", "split", "packed", "repacked", "small-packed"]),   # 64 passes
     (2, 40, K_MAX, ["auto", "repacked"]),
     (9, 64, K_MAX, ["auto", "split", "repacked", "small-packed"]),             # skinny tiles
     (130, 64, K_MAX, ["auto", "tile", "tile-mx"]),             # skinny above 64 rows, both tiles

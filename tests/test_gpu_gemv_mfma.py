@@ -67,21 +67,48 @@ SHAPES = [
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_shapes_against_oracle(dev, M, N, K):
     say(f"gemv_mfma M={M} N={N} K={K}")
-    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_MFMA
+    # from 5 rows on weights of at least 4096 x 4096 the skinny kernel runs
+    big = M >= 5 and N >= 4096 and K >= 4096
+    want = binding.W4A16_GEMV_SKINNY if big else binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(M, N, K) == want
     X, W = workloads.random_case(M, N, K, seed=N * 7 + K + M)
     qw, sc = oracle.quantize(W)
     check(run(X, qw, sc, dev), X, qw, sc, f"mfma {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
-def test_first_k_past_the_kernel(dev, M):
-    # past K = 8192: the fp32 GEMV for M <= 2, the skinny matrix-core kernel above
-    N, K = 70, 8192 + 32
-    want = binding.W4A16_GEMV_FMA if M <= 2 else binding.W4A16_GEMV_SKINNY
-    assert binding.w4a16_gemv_kernel(M, N, K) == want
-    X, W = workloads.random_case(M, N, K, seed=5)
+# past K = 8192 (256 groups): 8 waves take blocks of 16 groups in turn, so a
+# wave makes several passes; the first K past one pass, a last pass with one
+# group, passes that end inside a wave's block, and the longest K
+LONG_K = [(70, 8192 + 32), (33, 8192 + 4096 + 32), (129, 38144), (20, 1 << 17)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("N,K", LONG_K)
+def test_long_k_passes(dev, M, N, K):
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_MFMA
+    say(f"gemv_mfma long K M={M} N={N} K={K}")
+    X, W = workloads.random_case(M, N, K, seed=M + N + K)
     qw, sc = oracle.quantize(W)
-    check(run(X, qw, sc, dev), X, qw, sc, f"fp32 kernel {M}x{N}x{K}")
+    check(run(X, qw, sc, dev), X, qw, sc, f"mfma long K {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_long_k_swiglu_and_repacked(dev, M):
+    # the fused SwiGLU form and the repacked weights take the same passes; the
+    # repacked result equals the public layout's bit for bit
+    F, K = 40, 8192 + 4096 + 32
+    X, W = workloads.random_case(M, 2 * F, K, seed=M + 77)
+    qw, sc = oracle.quantize(W)
+    Ys = binding.w4a16_gemm_swiglu(to_dev(X, dev), to_dev(qw, dev), to_dev(sc, dev))
+    torch.cuda.synchronize()
+    v = oracle.compare_swiglu(Ys.cpu().numpy(), X, qw, sc)
+    assert v["ok"], v
+    Y = run(X, qw, sc, dev)
+    check(Y, X, qw, sc, f"mfma long K {M}x{2 * F}x{K}")
+    packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
+    Yr = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, 2 * F)
+    torch.cuda.synchronize()
+    assert np.array_equal(Yr.cpu().numpy().view(np.uint32), Y.view(np.uint32))
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 7])

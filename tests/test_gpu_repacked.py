@@ -1,9 +1,8 @@
 """GPU parity of the repack entry points against the oracle, through the C ABI:
 w4a16_repack must write the oracle's pack_grouped layout (one expert) byte for
 byte, and w4a16_gemm_repacked (the matrix-core decode GEMV of w4a16_gemm for
-M <= 8 and K <= 8192, bit for bit its result on the public layout; the
-split-K decode GEMV for M <= 4 with longer K when its LDS holds the
-activation limbs; otherwise the skinny kernel or the 128 x 128 matrix-core
+M <= 8, bit for bit its result on the public layout; otherwise the skinny
+kernel or the 128 x 128 matrix-core
 tile, whichever w4a16_select_path picks) must meet the tolerance on every
 output."""
 
@@ -58,14 +57,12 @@ def test_repack_matches_oracle_bytes(dev, N, K):
 
 
 SHAPES = [
-    # matrix-core decode GEMV (M <= 8, K <= 8192)
+    # matrix-core decode GEMV (M <= 8; past K = 8192 in several passes)
     (1, 512, 256), (2, 70, 224), (3, 33, 96), (4, 129, 512), (1, 16, 32), (2, 300, 7168),
-    (5, 17, 32), (8, 100, 1056),
-    # split-K decode GEMV (M <= 4, K > 8192, limbs fit its LDS)
-    (1, 100, 38144), (4, 64, 9344),
-    # skinny kernel (K too long for the split-K decode kernel's LDS, 9..64 rows,
-    # and above 64 rows while its rounds cost less than the tile's)
-    (1, 40, 38176), (4, 20, 9376), (17, 70, 160), (33, 45, 4128), (63, 33, 96), (64, 300, 7168),
+    (5, 17, 32), (8, 100, 1056), (1, 100, 38144), (4, 64, 9344), (1, 40, 38176), (4, 20, 9376),
+    # skinny kernel (9..64 rows, and above 64 rows while its rounds cost less
+    # than the tile's)
+    (17, 70, 160), (33, 45, 4128), (63, 33, 96), (64, 300, 7168),
     (65, 129, 224), (130, 200, 320), (300, 260, 256), (1100, 1300, 32),
 ]
 

@@ -1,5 +1,5 @@
-"""GPU parity of the skinny matrix-core kernel (W4A16_GEMV_SKINNY: M >= 3
-outside the decode GEMV's range), the kernel w4a16_gemm runs for the
+"""GPU parity of the skinny matrix-core kernel (W4A16_GEMV_SKINNY: M >= 9,
+past the decode GEMV's rows), the kernel w4a16_gemm runs for the
 tree-verification batches and, above 64 rows, while its rounds cost less than
 the 128 x 128 tile's, against the CPU oracle through the C ABI."""
 
@@ -64,11 +64,11 @@ def test_shapes_against_oracle(dev, M, N, K):
     check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
 
 
-# above 64 rows: one to many row blocks, the last one ragged; NT = 4, 2 and 1
-# column tiles per workgroup (N from 33 to 4096); group counts past and short
-# of a whole step
+# above 64 rows: one to many row blocks (up to 4375), the last one ragged;
+# NT = 4, 2 and 1 column tiles per workgroup (N from 20 to 4096); group counts
+# past and short of a whole step
 WIDE = [(65, 300, 2080), (65, 2048, 224), (80, 4096, 96), (130, 129, 224), (300, 260, 256), (513, 70, 4128),
-        (1000, 33, 160), (777, 1030, 32)]
+        (1000, 33, 160), (777, 1030, 32), (70000, 20, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", WIDE)
@@ -79,6 +79,19 @@ def test_above_64_rows_every_output(dev, M, N, K):
     X, W = workloads.random_case(M, N, K, seed=M * 17 + N + K)
     qw, sc = oracle.quantize(W)
     check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (8, 4096, 7168), (6, 4100, 4128)])
+def test_five_to_eight_rows_on_large_weights(dev, M, N, K):
+    # the decode GEMV's 8-row form loses to the skinny kernel here
+    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_SKINNY
+    X, W = workloads.random_case(M, N, K, seed=M * 5 + N + K)
+    qw, sc = oracle.quantize(W)
+    check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
+    packed = binding.w4a16_repack(to_dev(qw, dev), to_dev(sc, dev))
+    Yr = binding.w4a16_gemm_repacked(to_dev(X, dev), packed, N)
+    torch.cuda.synchronize()
+    check(Yr.cpu().numpy(), X, qw, sc, f"skinny repacked {M}x{N}x{K}")
 
 
 def test_forced_where_the_tile_wins(dev):
@@ -107,15 +120,6 @@ def test_above_64_rows_integer_exact_and_nonfinite(dev):
     assert np.all(np.isnan(Y[70])) and np.all(np.isnan(Y[199]))
     keep = [m for m in range(M) if m not in (70, 199)]
     assert np.array_equal(Y[keep].astype(np.float64), oracle.gemm(X[keep], qw, sc))
-
-
-@pytest.mark.parametrize("M", [3, 5, 8])
-def test_small_m_past_the_decode_gemv(dev, M):
-    N, K = 100, 8192 + 96
-    assert binding.w4a16_gemv_kernel(M, N, K) == binding.W4A16_GEMV_SKINNY
-    X, W = workloads.random_case(M, N, K, seed=M + 3)
-    qw, sc = oracle.quantize(W)
-    check(run(X, qw, sc, dev), X, qw, sc, f"skinny {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 96, 7168), (20, 50, 224), (40, 33, 2048)])

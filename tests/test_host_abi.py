@@ -42,13 +42,20 @@ def test_status_strings(lib):
 
 
 def test_gemv_kernel(lib):
-    # matrix-core decode GEMV for M <= 8 and K <= 8192; the skinny matrix-core
-    # kernel for M >= 3 otherwise; the fp32 FMA GEMV for M <= 2 with long K
+    # matrix-core decode GEMV for M <= 8 at any K; the skinny matrix-core
+    # kernel from 9 rows on; the fp32 FMA GEMV is never the automatic choice
     assert binding.w4a16_gemv_kernel(1, 4096, 7168) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(2, 7, 8192) == binding.W4A16_GEMV_MFMA
-    assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_FMA
-    assert binding.w4a16_gemv_kernel(2, 64, 1 << 17) == binding.W4A16_GEMV_FMA
-    assert binding.w4a16_gemv_kernel(3, 64, 8192 + 32) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(1, 64, 8192 + 32) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(2, 64, 1 << 17) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(3, 64, 8192 + 32) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(8, 64, 1 << 17) == binding.W4A16_GEMV_MFMA
+    # 5..8 rows on weights of at least 4096 x 4096: the skinny kernel
+    assert binding.w4a16_gemv_kernel(4, 4096, 7168) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(5, 4096, 4096) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(8, 14336, 4096) == binding.W4A16_GEMV_SKINNY
+    assert binding.w4a16_gemv_kernel(8, 4095, 7168) == binding.W4A16_GEMV_MFMA
+    assert binding.w4a16_gemv_kernel(8, 4096, 4064) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(4, 64, 256) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(8, 64, 256) == binding.W4A16_GEMV_MFMA
     assert binding.w4a16_gemv_kernel(9, 64, 256) == binding.W4A16_GEMV_SKINNY
