@@ -406,11 +406,12 @@ size_t w4a16_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * tolerance of w4a16_gemm holds for rows whose magnitudes span up to about
  * 2^22; a row spanning 2^26 or more whose largest entries meet zero weights
  * can leave it.  The same holds for the other entry points on this arithmetic
- * (w4a16_gemm_split_packed, w4a16_gemm_grouped(_packed), w4a16_gemm_repacked,
+ * (w4a16_gemm_split_packed, w4a16_gemm_grouped(_packed),
  * w4a16_gemm_small_packed(_noalloc), the last per row and K slice).
- * w4a16_gemm's own limb kernels (W4A16_GEMV_MFMA, W4A16_GEMV_SKINNY) take a
- * power of two per row and one or two groups of 32 and carry the low limb
- * x2^11, which keeps the tolerance for rows spanning 2^30 and more.
+ * w4a16_gemm's own limb kernels (W4A16_GEMV_MFMA, W4A16_GEMV_SKINNY,
+ * W4A16_PATH_TILE_MX), which w4a16_gemm_repacked runs as well, take a power
+ * of two per row and one or two groups of 32 and carry the low limb x2^11,
+ * which keeps the tolerance for rows spanning 2^30 and more.
  *
  * `workspace` is a DEVICE buffer owned by the caller, 256-byte aligned, of at
  * least w4a16_split_workspace_bytes(M, N, K) bytes, not overlapping any other
