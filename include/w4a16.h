@@ -196,9 +196,11 @@ int w4a16_gemm_repacked(const float *X, const void *packed, float *Y, int64_t M,
  *     silu(g) = g / (1 + exp(-g)),
  * with g and u the same fp32 group-scaled sums as w4a16_gemm and the epilogue
  * in fp32.  Y is [M][F] (not 2F); the gate/up outputs never reach memory.
- * Runs on the matrix-core decode GEMV for M <= 8 and on the fp32 FMA GEMV
- * above (any M accepted; the skinny kernel has no fused form).  Errors as
- * w4a16_gemm with N = 2F.
+ * Runs on the kernel w4a16_gemv_kernel(M, 2F, K) names: the matrix-core
+ * decode GEMV, or else the skinny kernel's fused form (any M accepted: each
+ * workgroup computes the gate and the up tiles of the same 16 x 32 or 16 x 16
+ * outputs and stores the product).
+ * Errors as w4a16_gemm with N = 2F.
  */
 int w4a16_gemm_swiglu(const float *X, const int32_t *qweight, const float *scales, float *Y,
                       int64_t M, int64_t F, int64_t K, int32_t group, void *stream);

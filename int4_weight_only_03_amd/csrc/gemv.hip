@@ -45,29 +45,15 @@ constexpr int kLoaders = 128;       // activation-staging threads per block (fas
 constexpr int kXChunk = 16;         // float4 each staging thread moves (32 KB per block)
 constexpr int kFastMaxLds = 64 * 1024;
 
-// Rows of W a thread handles.  Plain GEMV: logical row = W row, RB of them.
-// Fused gate/up SwiGLU (kSw): W holds 2F rows (gate rows 0..F-1, then up rows
-// F..2F-1); the thread's RB rows are RB/2 logical rows n, loaded as gate row n
-// (i < RB/2) and up row F + n (i >= RB/2), and each output is
-// silu(gate) * up with silu(g) = g / (1 + exp(-g)).
-template <bool kSw, int RB>
-__device__ __forceinline__ long w_row(long rowbase, int slot, int i, int S, long N) {
-  constexpr int RBL = kSw ? RB / 2 : RB;
-  const long nl = rowbase + slot + long(i % RBL) * S;
-  return (kSw && i >= RBL) ? nl + N / 2 : nl;
-}
-
 
 // Fast kernel (M = MT).  Thread t < kLoaders stages the MT rows of X in LDS;
 // thread kLoaders + s*G + c (c < G, s < S) is compute thread (slot s, group
 // c) for rows rowbase + s + i*S, i < RB.  Z (16, 32 or 64) divides G, so
 // segments of Z compute lanes never straddle a slot.
-template <int MT, int RB, int Z, bool kSw>
+template <int MT, int RB, int Z>
 __global__ void __launch_bounds__(kFastMaxBlock)
 gemv_ws(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *__restrict__ sc,
         float *__restrict__ Y, int M, int N, int G, int S) {
-  constexpr int RBL = kSw ? RB / 2 : RB;  // logical rows per slot
-  static_assert(!kSw || RB % 2 == 0, "gate/up pairs");
   extern __shared__ __align__(16) float lds[];
   const long K = long(G) * kGroup;
   const int rowx4 = G * 8;            // float4 per activation row
@@ -81,7 +67,7 @@ gemv_ws(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   const bool active = !loader && slot0 < S;
   const int slot = active ? slot0 : 0;
   const int g = active ? c - slot0 * G : 0;
-  const long rowbase = long(blockIdx.x) * S * RBL;
+  const long rowbase = long(blockIdx.x) * S * RB;
   float acc[MT][RB];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -107,7 +93,7 @@ gemv_ws(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   } else {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {  // clamped rows: no branch between loads
-      const long n = std::min(w_row<kSw, RB>(rowbase, slot, i, S, N), long(N) - 1);
+      const long n = std::min(rowbase + slot + long(i) * S, long(N) - 1);
       w[i] = load_stream16(qw + n * G + g);
       s[i] = load_stream4(sc + n * G + g);
     }
@@ -145,19 +131,15 @@ gemv_ws(const float *__restrict__ X, const uint4 *__restrict__ qw, const float *
   }
   __syncthreads();
   const int sps = G / Z;  // segments per slot
-  const long NY = kSw ? N / 2 : N;  // outputs per row of Y
-  for (int o = t; o < S * MT * RBL; o += blockDim.x) {
-    const int sl = o / (MT * RBL);
-    const int r = o - sl * (MT * RBL);
-    const int m = r / RBL;
-    const int i = r - m * RBL;
-    float v = 0.0f, u = 0.0f;
-    for (int k = 0; k < sps; ++k) {
-      v += part[(sl * sps + k) * (MT * RB) + m * RB + i];
-      if (kSw) u += part[(sl * sps + k) * (MT * RB) + m * RB + i + RBL];
-    }
+  for (int o = t; o < S * MT * RB; o += blockDim.x) {
+    const int sl = o / (MT * RB);
+    const int r = o - sl * (MT * RB);
+    const int m = r / RB;
+    const int i = r - m * RB;
+    float v = 0.0f;
+    for (int k = 0; k < sps; ++k) v += part[(sl * sps + k) * (MT * RB) + m * RB + i];
     const long n = rowbase + sl + long(i) * S;
-    if (m < M && n < NY) Y[long(m) * NY + n] = kSw ? silu_mul(v, u) : v;
+    if (m < M && n < N) Y[long(m) * N + n] = v;
   }
 }
 
@@ -167,23 +149,20 @@ struct FastPlan {
 };
 
 // Fast kernel plan: about one block per compute unit (256 on MI355X).
-bool plan_fast(int M, int N, int G, bool sw, FastPlan &p) {
+bool plan_fast(int M, int N, int G, FastPlan &p) {
   if (M > 2) return false;
-  const long NL = sw ? N / 2 : N;  // logical rows (outputs per row of Y)
   p.MT = M;  // the fast kernel stages all M rows at once
   p.Z = 1;
   while (p.Z < 64 && G % (2 * p.Z) == 0) p.Z *= 2;
   if (p.Z < 16) return false;  // segments of 16, 32 or 64 lanes only
   const int s_max = (kFastMaxBlock - kLoaders) / G;
   if (s_max < 1) return false;
-  const long rows_per_block = std::max(1L, (NL + 255) / 256);
+  const long rows_per_block = std::max(1L, (long(N) + 255) / 256);
   const int prefs[4] = {4, 8, 2, 1};
   p.RB = 0;
   for (int rb : prefs) {
     if (rb * p.MT > 8) continue;  // MT*RB <= 8 partial sums keeps the kernel spill-free
-    if (sw && rb < 2) continue;   // gate/up pairs
-    const int rbl = sw ? rb / 2 : rb;
-    const long s = (rows_per_block + rbl - 1) / rbl;
+    const long s = (rows_per_block + rb - 1) / rb;
     if (s <= s_max) {
       p.RB = rb;
       p.S = int(s);
@@ -194,49 +173,43 @@ bool plan_fast(int M, int N, int G, bool sw, FastPlan &p) {
     p.RB = 8 / p.MT;
     p.S = s_max;
   }
-  const int rbl = sw ? p.RB / 2 : p.RB;
   if (long(p.MT) * G * 8 > long(kLoaders) * kXChunk) return false;  // one staging pass
   p.BS = ((kLoaders + p.S * G + 63) / 64) * 64;
-  p.blocks = int((NL + long(p.S) * rbl - 1) / (long(p.S) * rbl));
+  p.blocks = int((long(N) + long(p.S) * p.RB - 1) / (long(p.S) * p.RB));
   const size_t segs = size_t(p.BS - kLoaders) / p.Z + 1;
   p.lds = 16 * (size_t(p.MT) * G * 8 + 1) + segs * p.MT * p.RB * sizeof(float);
   return p.lds <= size_t(kFastMaxLds);
 }
 
-template <int MT, int RB, int Z, bool kSw>
+template <int MT, int RB, int Z>
 hipError_t run_fast(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
                     float *Y, int M, int N, int G, hipStream_t stream) {
-  if constexpr (kSw && RB % 2 != 0) {
-    return hipErrorInvalidValue;
-  } else {
-    hipLaunchKernelGGL((gemv_ws<MT, RB, Z, kSw>), dim3(p.blocks), dim3(p.BS), p.lds, stream, X,
-                       reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G, p.S);
-    return hipGetLastError();
-  }
+  hipLaunchKernelGGL((gemv_ws<MT, RB, Z>), dim3(p.blocks), dim3(p.BS), p.lds, stream, X,
+                     reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G, p.S);
+  return hipGetLastError();
 }
 
-template <int Z, bool kSw>
+template <int Z>
 hipError_t dispatch_fast_z(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
                            float *Y, int M, int N, int G, hipStream_t stream) {
   switch (p.MT * 16 + p.RB) {
-    case 1 * 16 + 8: return run_fast<1, 8, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 4: return run_fast<1, 4, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 2: return run_fast<1, 2, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 1: return run_fast<1, 1, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 4: return run_fast<2, 4, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 2: return run_fast<2, 2, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 1: return run_fast<2, 1, Z, kSw>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 8: return run_fast<1, 8, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 4: return run_fast<1, 4, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 2: return run_fast<1, 2, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 1: return run_fast<1, 1, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 4: return run_fast<2, 4, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 2: return run_fast<2, 2, Z>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 1: return run_fast<2, 1, Z>(p, X, qw, sc, Y, M, N, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool kSw>
 hipError_t dispatch_fast(const FastPlan &p, const float *X, const int32_t *qw, const float *sc,
                          float *Y, int M, int N, int G, hipStream_t stream) {
   switch (p.Z) {
-    case 64: return dispatch_fast_z<64, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 32: return dispatch_fast_z<32, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 16: return dispatch_fast_z<16, kSw>(p, X, qw, sc, Y, M, N, G, stream);
+    case 64: return dispatch_fast_z<64>(p, X, qw, sc, Y, M, N, G, stream);
+    case 32: return dispatch_fast_z<32>(p, X, qw, sc, Y, M, N, G, stream);
+    case 16: return dispatch_fast_z<16>(p, X, qw, sc, Y, M, N, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -249,13 +222,11 @@ hipError_t dispatch_fast(const FastPlan &p, const float *X, const int32_t *qw, c
 
 constexpr int kMaxBlock = 512;  // 8 waves per block leaves up to 256 VGPRs per lane
 
-template <int MT, int RB, bool kSw>
+template <int MT, int RB>
 __global__ void __launch_bounds__(kMaxBlock)
 gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
            const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G, int S,
            int TPS, int T) {
-  constexpr int RBL = kSw ? RB / 2 : RB;  // logical rows per slot
-  static_assert(!kSw || RB % 2 == 0, "gate/up pairs");
   extern __shared__ float red[];  // [MT*RB][blockDim.x + 1]
   const int BS = blockDim.x;
   const int ld = BS + 1;
@@ -263,9 +234,8 @@ gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
   const int slot = t / TPS;
   const int col = t - slot * TPS;
   const bool active = slot < S;
-  const long rowbase = long(blockIdx.x) * S * RBL;
+  const long rowbase = long(blockIdx.x) * S * RB;
   const long K = long(G) * kGroup;
-  const long NY = kSw ? N / 2 : N;  // outputs per row of Y
 
   for (int m0 = 0; m0 < M; m0 += MT) {
     float acc[MT][RB];
@@ -280,7 +250,7 @@ gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
         float s[RB];
 #pragma unroll
         for (int i = 0; i < RB; ++i) {  // clamped rows: no branch between loads
-          const long n = std::min(w_row<kSw, RB>(rowbase, slot, i, S, N), long(N) - 1);
+          const long n = std::min(rowbase + slot + long(i) * S, long(N) - 1);
           w[i] = load_stream16(qw + n * G + g);
           s[i] = load_stream4(sc + n * G + g);
         }
@@ -310,27 +280,21 @@ gemv_w4a16(const float *__restrict__ X, const uint4 *__restrict__ qw,
       for (int i = 0; i < RB; ++i) red[(m * RB + i) * ld + t] = acc[m][i];
     __syncthreads();
 
-    const int O = MT * S * RBL;  // outputs of this block and m-tile
+    const int O = MT * S * RB;  // outputs of this block and m-tile
     const int team = t / T;
     const int j = t - team * T;
     const int teams = BS / T;
     for (int o = team; o < O; o += teams) {
-      const int m = o / (S * RBL);
-      const int r = o - m * S * RBL;
+      const int m = o / (S * RB);
+      const int r = o - m * S * RB;
       const int i = r / S;
       const int sl = r - i * S;
       const float *src = red + (m * RB + i) * ld + sl * TPS;
       float v = 0.0f;
       for (int c = j; c < TPS; c += T) v += src[c];
       for (int d = T >> 1; d > 0; d >>= 1) v += __shfl_xor(v, d, T);
-      float u = 0.0f;
-      if (kSw) {
-        const float *src_u = red + (m * RB + i + RBL) * ld + sl * TPS;
-        for (int c = j; c < TPS; c += T) u += src_u[c];
-        for (int d = T >> 1; d > 0; d >>= 1) u += __shfl_xor(u, d, T);
-      }
       const long n = rowbase + sl + long(i) * S;
-      if (j == 0 && m0 + m < M && n < NY) Y[long(m0 + m) * NY + n] = kSw ? silu_mul(v, u) : v;
+      if (j == 0 && m0 + m < M && n < N) Y[long(m0 + m) * N + n] = v;
     }
     __syncthreads();
   }
@@ -349,17 +313,15 @@ int pow2_floor(int v) {
 // 256 CUs x ~7 resident waves: enough 16-byte loads in flight to cover HBM latency.
 constexpr long kTargetThreads = 256L * 7 * 64;
 
-GemvPlan plan_gemv(int M, int N, int G, bool sw) {
+GemvPlan plan_gemv(int M, int N, int G) {
   GemvPlan p;
-  const long NL = sw ? N / 2 : N;  // logical rows (outputs per row of Y)
   p.TPS = std::min(G, kMaxBlock);
   p.MT = M >= 3 ? 4 : (M == 2 ? 2 : 1);
   // Rows per thread: as many as keep ~kTargetThreads threads busy (amortizes
   // the activation loads), at least 1.
   const long chunks = long(N) * p.TPS;
   p.RB = 8 / p.MT;  // MT*RB <= 8 partial sums per thread keeps VGPRs below 256
-  while (p.RB > (sw ? 2 : 1) && chunks / p.RB < kTargetThreads) p.RB /= 2;
-  const int rbl = sw ? p.RB / 2 : p.RB;
+  while (p.RB > 1 && chunks / p.RB < kTargetThreads) p.RB /= 2;
   // Slots per block: the count with the fewest idle lanes in whole waves,
   // the smaller count on ties.
   int best_s = 1, best_idle = 1 << 30;
@@ -373,51 +335,44 @@ GemvPlan plan_gemv(int M, int N, int G, bool sw) {
   }
   p.S = best_s;
   p.BS = ((p.S * p.TPS + 63) / 64) * 64;
-  p.blocks = int((NL + long(p.S) * rbl - 1) / (long(p.S) * rbl));
-  const int O = p.MT * p.S * rbl;
+  p.blocks = int((long(N) + long(p.S) * p.RB - 1) / (long(p.S) * p.RB));
+  const int O = p.MT * p.S * p.RB;
   p.T = std::min(64, std::max(1, pow2_floor(std::max(1, p.BS / O))));
   return p;
 }
 
-template <int MT, int RB, bool kSw>
+template <int MT, int RB>
 hipError_t run(const GemvPlan &p, const float *X, const int32_t *qw, const float *sc, float *Y,
                int M, int N, int G, hipStream_t stream) {
   if (p.MT != MT || p.RB != RB) return hipErrorInvalidValue;  // plan and kernel must agree
-  if constexpr (kSw && RB % 2 != 0) {
-    return hipErrorInvalidValue;
-  } else {
-    const size_t lds = size_t(MT) * RB * (p.BS + 1) * sizeof(float);
-    hipLaunchKernelGGL((gemv_w4a16<MT, RB, kSw>), dim3(p.blocks), dim3(p.BS), lds, stream, X,
-                       reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G, p.S, p.TPS, p.T);
-    return hipGetLastError();
-  }
+  const size_t lds = size_t(MT) * RB * (p.BS + 1) * sizeof(float);
+  hipLaunchKernelGGL((gemv_w4a16<MT, RB>), dim3(p.blocks), dim3(p.BS), lds, stream, X,
+                     reinterpret_cast<const uint4 *>(qw), sc, Y, M, N, G, p.S, p.TPS, p.T);
+  return hipGetLastError();
 }
 
-template <bool kSw>
 hipError_t dispatch(const GemvPlan &p, const float *X, const int32_t *qw, const float *sc,
                     float *Y, int M, int N, int G, hipStream_t stream) {
   switch (p.MT * 16 + p.RB) {
-    case 1 * 16 + 8: return run<1, 8, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 4: return run<1, 4, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 2: return run<1, 2, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 1 * 16 + 1: return run<1, 1, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 4: return run<2, 4, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 2: return run<2, 2, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 2 * 16 + 1: return run<2, 1, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 4 * 16 + 2: return run<4, 2, kSw>(p, X, qw, sc, Y, M, N, G, stream);
-    case 4 * 16 + 1: return run<4, 1, kSw>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 8: return run<1, 8>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 4: return run<1, 4>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 2: return run<1, 2>(p, X, qw, sc, Y, M, N, G, stream);
+    case 1 * 16 + 1: return run<1, 1>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 4: return run<2, 4>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 2: return run<2, 2>(p, X, qw, sc, Y, M, N, G, stream);
+    case 2 * 16 + 1: return run<2, 1>(p, X, qw, sc, Y, M, N, G, stream);
+    case 4 * 16 + 2: return run<4, 2>(p, X, qw, sc, Y, M, N, G, stream);
+    case 4 * 16 + 1: return run<4, 1>(p, X, qw, sc, Y, M, N, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool kSw>
 hipError_t launch(const float *X, const int32_t *qweight, const float *scales, float *Y, int M,
                   int N, int K, hipStream_t stream) {
   const int G = K / kGroup;
   FastPlan fp;
-  if (plan_fast(M, N, G, kSw, fp))
-    return dispatch_fast<kSw>(fp, X, qweight, scales, Y, M, N, G, stream);
-  return dispatch<kSw>(plan_gemv(M, N, G, kSw), X, qweight, scales, Y, M, N, G, stream);
+  if (plan_fast(M, N, G, fp)) return dispatch_fast(fp, X, qweight, scales, Y, M, N, G, stream);
+  return dispatch(plan_gemv(M, N, G), X, qweight, scales, Y, M, N, G, stream);
 }
 
 }  // namespace
@@ -442,20 +397,22 @@ hipError_t launch_gemv(const float *X, const int32_t *qweight, const float *scal
   switch (gemv_kernel(M, N, K)) {
     case W4A16_GEMV_MFMA: return launch_gemv_mfma(X, qweight, scales, Y, M, N, K, stream);
     case W4A16_GEMV_SKINNY: return launch_skinny(X, qweight, scales, Y, M, N, K, stream);
-    default: return launch<false>(X, qweight, scales, Y, M, N, K, stream);
+    default: return launch(X, qweight, scales, Y, M, N, K, stream);
   }
 }
 
 hipError_t launch_gemv_fma(const float *X, const int32_t *qweight, const float *scales, float *Y,
                            int M, int N, int K, hipStream_t stream) {
-  return launch<false>(X, qweight, scales, Y, M, N, K, stream);
+  return launch(X, qweight, scales, Y, M, N, K, stream);
 }
 
 hipError_t launch_gemv_swiglu(const float *X, const int32_t *qweight, const float *scales,
                               float *Y, int M, int F, int K, hipStream_t stream) {
-  if (gemv_mfma_supported(M, K))  // matrix-core decode GEMV (gemv_mfma.hip)
+  // the same choice as launch_gemv over the 2F rows of W (measured: 15.0
+  // against 18.8 us at 8 x 2*2048 x 7168 on the skinny kernel's fused form)
+  if (gemv_kernel(M, 2 * F, K) == W4A16_GEMV_MFMA)  // matrix-core decode GEMV (gemv_mfma.hip)
     return launch_gemv_mfma_swiglu(X, qweight, scales, Y, M, F, K, stream);
-  return launch<true>(X, qweight, scales, Y, M, 2 * F, K, stream);
+  return launch_skinny_swiglu(X, qweight, scales, Y, M, F, K, stream);  // skinny.hip
 }
 
 }  // namespace w4a16

@@ -81,7 +81,11 @@ __device__ __forceinline__ void sk_wait_lgkm0() {
 // uses (and their zero extension) inside the loop.
 __device__ __forceinline__ void sk_opaque(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-template <int MT, int NT, int P, bool kRP>
+// kSw: fused gate/up SwiGLU (public layout): W holds 2N rows, gate rows
+// 0..N-1 then up rows N..2N-1; a workgroup's first NT/2 column tiles are gate
+// rows and its last NT/2 the up rows of the same outputs, and the store
+// writes silu(gate) * up.
+template <int MT, int NT, int P, bool kRP, bool kSw = false>
 __global__ void __launch_bounds__(64 * kSkWaves)
 skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
           const float *__restrict__ sc, float *__restrict__ Y, int M, int N, int G,
@@ -108,7 +112,9 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int c = lane & 15, R = lane >> 4;
   const int nb = blockIdx.x % tiles_n, mb = blockIdx.x / tiles_n;
-  const int m0 = mb * 16 * MT, n0 = nb * 16 * NT;
+  static_assert(!kSw || (!kRP && NT % 2 == 0), "SwiGLU: public layout, gate and up tiles");
+  constexpr int NO = kSw ? NT / 2 : NT;  // output column tiles
+  const int m0 = mb * 16 * MT, n0 = nb * 16 * NO;
   const int S = G / SG;  // whole steps
   const int s0 = int(long(S) * wave / kSkWaves), s1 = int(long(S) * (wave + 1) / kSkWaves);
   // this wave's staging slot of ring entry v
@@ -143,12 +149,16 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
   uint32_t woff[NT], soff[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const uint32_t wrow = uint32_t(std::min(n0 + 16 * t + lane / 4, N - 1) - n0);
+    const int to = t % NO;  // the output tile (kSw: gate tiles, then up tiles)
+    const uint32_t wrow = uint32_t(std::min(n0 + 16 * to + lane / 4, N - 1) - n0);
     woff[t] = (wrow * uint32_t(G) + uint32_t(wg)) * 16u;
     soff[t] = (wrow * uint32_t(G) + uint32_t(lane & 3)) * 4u;
   }
   const char *wtile = reinterpret_cast<const char *>(qw) + long(n0) * G * 16;
   const char *stile = reinterpret_cast<const char *>(sc) + long(n0) * G * 4;
+  // kSw: the up rows sit N rows further
+  const char *wtile_u = wtile + (kSw ? long(N) * G * 16 : 0);
+  const char *stile_u = stile + (kSw ? long(N) * G * 4 : 0);
   // kRP: qw is w4a16_repack's buffer, a 1 KB block per (16-row tile, 4-group
   // step) with lane l's 16 bytes its operand words for the 4 groups (word
   // l / 16 of each, row l % 16), then a 256-byte block of the 16 rows' 4
@@ -198,10 +208,10 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
       if constexpr (!kRP) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const char *wsrc = wtile + gs * 16 + woff[t];
+          const char *wsrc = (t < NO ? wtile : wtile_u) + gs * 16 + woff[t];
           __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0,
                                            0);
-          const char *ssrc = stile + gs * 4 + soff[t];
+          const char *ssrc = (t < NO ? stile : stile_u) + gs * 4 + soff[t];
           __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
         }
       }
@@ -220,10 +230,11 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
         const long gsc = std::min(gs + (lane & 3), long(G) - 1);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const char *wsrc = wtile + gw * 16 + (woff[t] - 16u * uint32_t(wg));
+          const char *wsrc = (t < NO ? wtile : wtile_u) + gw * 16 + (woff[t] - 16u * uint32_t(wg));
           __builtin_amdgcn_global_load_lds(wsrc, (sk_lds_void *)(slot + kWOff + 1024 * t), 16, 0,
                                            0);
-          const char *ssrc = stile + gsc * 4 + (soff[t] - 4u * uint32_t(lane & 3));
+          const char *ssrc =
+              (t < NO ? stile : stile_u) + gsc * 4 + (soff[t] - 4u * uint32_t(lane & 3));
           __builtin_amdgcn_global_load_lds(ssrc, (sk_lds_void *)(slot + kSOff + 256 * t), 4, 0, 0);
         }
       }
@@ -447,15 +458,33 @@ skinny_mx(const float *__restrict__ X, const uint32_t *__restrict__ qw,
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave * kTile + ((u * NT + t) * 4 + r) * 64 + lane] = acc[u][t][r];
   __syncthreads();
-  for (int i = threadIdx.x; i < kTile; i += 64 * kSkWaves) {
-    float v = 0.0f;
+  if constexpr (kSw) {
+    // gate tile t and up tile t + NO hold the same outputs
+    for (int i = threadIdx.x; i < MT * NO * 256; i += 64 * kSkWaves) {
+      const int l = i & 63, r = (i >> 6) & 3, ut = i >> 8;
+      const int u = ut / NO, t = ut - u * NO;
+      const int ig = ((u * NT + t) * 4 + r) * 64 + l, iu = ig + NO * 256;
+      float g = 0.0f, v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) v += red[w * kTile + i];
-    const int l = i & 63, r = (i >> 6) & 3, ut = i >> 8;
-    const int u = ut / NT, t = ut - u * NT;
-    const int m = m0 + 16 * u + 4 * (l >> 4) + r;
-    const int n = n0 + 16 * t + (l & 15);
-    if (m < M && n < N) Y[long(m) * N + n] = v;
+      for (int w = 0; w < kSkWaves; ++w) {
+        g += red[w * kTile + ig];
+        v += red[w * kTile + iu];
+      }
+      const int m = m0 + 16 * u + 4 * (l >> 4) + r;
+      const int n = n0 + 16 * t + (l & 15);
+      if (m < M && n < N) Y[long(m) * N + n] = silu_mul(g, v);
+    }
+  } else {
+    for (int i = threadIdx.x; i < kTile; i += 64 * kSkWaves) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSkWaves; ++w) v += red[w * kTile + i];
+      const int l = i & 63, r = (i >> 6) & 3, ut = i >> 8;
+      const int u = ut / NT, t = ut - u * NT;
+      const int m = m0 + 16 * u + 4 * (l >> 4) + r;
+      const int n = n0 + 16 * t + (l & 15);
+      if (m < M && n < N) Y[long(m) * N + n] = v;
+    }
   }
 }
 
@@ -539,6 +568,30 @@ hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *sc
 hipError_t launch_skinny_repacked(const float *X, const void *packed, float *Y, int M, int N,
                                   int K, hipStream_t stream) {
   return dispatch_skinny<true>(X, packed, nullptr, Y, M, N, K, stream);
+}
+
+// The fused SwiGLU form: W has 2F rows; workgroups of 16 rows of X by 16 NT/2
+// outputs (NT = 4 when that leaves at least 256 workgroups, else 2).
+hipError_t launch_skinny_swiglu(const float *X, const int32_t *qweight, const float *scales,
+                                float *Y, int M, int F, int K, hipStream_t stream) {
+  if (!skinny_supported(M)) return hipErrorInvalidValue;
+  const int G = K / kGroup;
+  SkPlan p;
+  p.MT = 1;
+  p.tiles_m = int((long(M) + 15) / 16);
+  p.NT = (long(F) + 31) / 32 * p.tiles_m >= 256 ? 4 : 2;
+  p.tiles_n = int((long(F) + 8 * p.NT - 1) / (8 * p.NT));
+  const long blocks = long(p.tiles_m) * p.tiles_n;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  if (p.NT == 4)
+    hipLaunchKernelGGL((skinny_mx<1, 4, kSkP, false, true>), dim3(unsigned(blocks)),
+                       dim3(64 * kSkWaves), 0, stream, X,
+                       reinterpret_cast<const uint32_t *>(qweight), scales, Y, M, F, G, p.tiles_n);
+  else
+    hipLaunchKernelGGL((skinny_mx<1, 2, kSkP, false, true>), dim3(unsigned(blocks)),
+                       dim3(64 * kSkWaves), 0, stream, X,
+                       reinterpret_cast<const uint32_t *>(qweight), scales, Y, M, F, G, p.tiles_n);
+  return hipGetLastError();
 }
 
 }  // namespace w4a16

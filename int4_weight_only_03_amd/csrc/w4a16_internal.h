@@ -45,6 +45,10 @@ bool skinny_supported(int M);
 bool skinny_preferred(int M, int N);
 hipError_t launch_skinny(const float *X, const int32_t *qweight, const float *scales, float *Y,
                          int M, int N, int K, hipStream_t stream);
+// the skinny kernel with the fused gate/up SwiGLU epilogue (W: 2F rows, gate
+// then up; Y[M][F])
+hipError_t launch_skinny_swiglu(const float *X, const int32_t *qweight, const float *scales,
+                                float *Y, int M, int F, int K, hipStream_t stream);
 // the skinny kernel on w4a16_repack's layout (one expert of the grouped pack)
 hipError_t launch_skinny_repacked(const float *X, const void *packed, float *Y, int M, int N,
                                   int K, hipStream_t stream);

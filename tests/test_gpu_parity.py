@@ -23,9 +23,9 @@ pytestmark = pytest.mark.gpu
 from int4_weight_only_03_amd import binding  # noqa: E402
 
 PACKED = -1  # the split path on weights repacked by w4a16_split_pack
-PATHS = {"gemv": binding.W4A16_PATH_GEMV, "tile": binding.W4A16_PATH_TILE,
-         "tile-mx": binding.W4A16_PATH_TILE_MX, "split": binding.W4A16_PATH_SPLIT,
-         "packed": PACKED}
+PATHS = {"gemv": binding.W4A16_PATH_GEMV, "gemv-fma": binding.W4A16_PATH_GEMV_FMA,
+         "tile": binding.W4A16_PATH_TILE, "tile-mx": binding.W4A16_PATH_TILE_MX,
+         "split": binding.W4A16_PATH_SPLIT, "packed": PACKED}
 
 
 def say(*a):
