@@ -80,7 +80,7 @@ PATH_SOURCES = {"gemv": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common
                 "gemv-fma": ["gemv.hip", "gemv_common.h"], "tile": ["tile.hip"],
                 "tile-mx": ["tile_mx.hip", "limbs.h"],
                 "split": ["split.hip", "limbs.h"], "packed": ["split.hip", "limbs.h"],
-                "swiglu": ["gemv.hip", "gemv_mfma.hip", "gemv_common.h", "limbs.h"],
+                "swiglu": ["gemv.hip", "gemv_mfma.hip", "skinny.hip", "gemv_common.h", "limbs.h"],
                 "grouped": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "grouped-packed": ["grouped.hip", "gemv_common.h", "limbs.h"],
                 "repacked": ["gemv_mfma.hip", "skinny.hip", "tile_mx.hip",
